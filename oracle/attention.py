@@ -1,0 +1,182 @@
+"""Oracle: tree attention forward and backward (test infrastructure only).
+
+The tree-training page (section "树构建过程", the attention-mask column of its
+figure) fixes the rule: a packed token attends only to its ancestors, itself
+included.  The Megatron integration (section "Megatron 引擎") states this as a
+dense attention-mask tensor; this module builds exactly that mask by walking
+parent chains and applies ordinary masked softmax attention to it, in float64.
+
+Readings of what the page leaves open:
+  * softmax scale 1/sqrt(head_dim) unless given;
+  * grouped-query attention: query head h reads key/value head h // (Hq/Hkv);
+  * LSE is the natural-log log-sum-exp of the scaled scores, laid out [Hq, Np];
+  * a pad row sees only itself (so its output is its own value row).
+
+Arrays: q [Np, Hq, d], k and v [Np, Hkv, d]; any real dtype, computed in float64.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional
+
+import numpy as np
+
+from .tree import Tree
+
+
+def ancestors(tree: Tree, i: int) -> np.ndarray:
+    """Keys visible to query i: its parent chain, itself included, ascending.
+    A pad row sees only itself."""
+    chain = []
+    j = i
+    if i >= tree.n_tokens:
+        return np.array([i], dtype=np.int64)
+    while j != -1:
+        chain.append(j)
+        j = int(tree.parent[j])
+    return np.array(chain[::-1], dtype=np.int64)
+
+
+def dense_mask(tree: Tree) -> np.ndarray:
+    """M[i, j] = True iff key j is on query i's parent chain (i included)."""
+    Np = tree.n_padded
+    M = np.zeros((Np, Np), dtype=bool)
+    for i in range(Np):
+        M[i, ancestors(tree, i)] = True
+    return M
+
+
+def _scale(d: int, scale: Optional[float]) -> float:
+    return 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+
+
+def _group(hq: int, hkv: int) -> int:
+    if hq % hkv:
+        raise ValueError(f"Hq={hq} is not a multiple of Hkv={hkv}")
+    return hq // hkv
+
+
+def _logsumexp(s: np.ndarray) -> np.ndarray:
+    m = s.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(s - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def attn_fwd(tree: Tree, q, k, v, scale=None, mask=None):
+    """O[i,h] = sum_j softmax_j(scale * q[i,h] . k[j,g]) v[j,g] over visible j.
+    Returns (O [Np,Hq,d] float64, LSE [Hq,Np] float64)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    Np, hq, d = q.shape
+    G = _group(hq, k.shape[1])
+    s = _scale(d, scale)
+    M = dense_mask(tree) if mask is None else mask
+    O = np.zeros_like(q)
+    LSE = np.zeros((hq, Np))
+    for h in range(hq):
+        g = h // G
+        S = s * (q[:, h, :] @ k[:, g, :].T)
+        S = np.where(M, S, -np.inf)
+        lse = _logsumexp(S)
+        P = np.exp(S - lse[:, None])
+        O[:, h, :] = P @ v[:, g, :]
+        LSE[h] = lse
+    return O, LSE
+
+
+def attn_bwd(tree: Tree, q, k, v, dout, scale=None, mask=None):
+    """Gradients of sum(dout * O) with respect to q, k, v (float64): the
+    softmax-attention vector-Jacobian product restricted to the tree mask;
+    each key/value head sums the contributions of the query heads that read it."""
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    Np, hq, d = q.shape
+    G = _group(hq, k.shape[1])
+    s = _scale(d, scale)
+    M = dense_mask(tree) if mask is None else mask
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in range(hq):
+        g = h // G
+        S = np.where(M, s * (q[:, h, :] @ k[:, g, :].T), -np.inf)
+        P = np.exp(S - _logsumexp(S)[:, None])
+        O = P @ v[:, g, :]
+        Drow = (dout[:, h, :] * O).sum(axis=1)
+        dv[:, g, :] += P.T @ dout[:, h, :]
+        dP = dout[:, h, :] @ v[:, g, :].T
+        dS = P * (dP - Drow[:, None])
+        dq[:, h, :] = s * (dS @ k[:, g, :])
+        dk[:, g, :] += s * (dS.T @ q[:, h, :])
+    return dq, dk, dv
+
+
+def attn_fwd_rows(tree: Tree, q, k, v, rows: Iterable[int], heads: Iterable[int],
+                  scale=None):
+    """The forward definition evaluated for selected (row, head) pairs only,
+    walking each row's parent chain.  Returns {(i, h): (o [d], lse)}."""
+    d = q.shape[2]
+    G = _group(q.shape[1], k.shape[1])
+    s = _scale(d, scale)
+    out = {}
+    for i in rows:
+        anc = ancestors(tree, int(i))
+        for h in heads:
+            g = h // G
+            qi = np.asarray(q[i, h, :], dtype=np.float64)
+            kk = np.asarray(k[anc, g, :], dtype=np.float64)
+            vv = np.asarray(v[anc, g, :], dtype=np.float64)
+            sc = s * (kk @ qi)
+            m = sc.max()
+            e = np.exp(sc - m)
+            out[(int(i), int(h))] = (e @ vv / e.sum(), m + math.log(e.sum()))
+    return out
+
+
+def attn_bwd_rows(tree: Tree, q, k, v, dout, dq_rows: Iterable[int],
+                  dkv_rows: Iterable[int], heads_of_group, scale=None):
+    """Backward definition for selected rows.
+
+    dq_rows: queries i for which dQ[i, h] is wanted, h in `heads_of_group`'s heads.
+    dkv_rows: keys j for which dK[j, g], dV[j, g] are wanted (g the group).
+    heads_of_group: (g, [query heads of group g]).
+    Every query that sees a requested key is evaluated from its parent chain.
+    Returns ({(i,h): dq}, {(j,g): (dk, dv)})."""
+    d = q.shape[2]
+    s = _scale(d, scale)
+    g, heads = heads_of_group
+    f64 = lambda x: np.asarray(x, dtype=np.float64)  # noqa: E731
+
+    def row_terms(i, h):
+        anc = ancestors(tree, i)
+        qi, doi = f64(q[i, h, :]), f64(dout[i, h, :])
+        kk, vv = f64(k[anc, g, :]), f64(v[anc, g, :])
+        sc = s * (kk @ qi)
+        p = np.exp(sc - sc.max())
+        p /= p.sum()
+        o = p @ vv
+        dp = vv @ doi
+        ds = p * (dp - doi @ o)
+        return anc, p, ds, qi, doi
+
+    dq = {}
+    for i in dq_rows:
+        for h in heads:
+            anc, p, ds, qi, doi = row_terms(int(i), h)
+            dq[(int(i), h)] = s * (ds @ f64(k[anc, g, :]))
+    kids = {}
+    for i in range(tree.n_tokens):
+        kids.setdefault(int(tree.parent[i]), []).append(i)
+    dkv = {}
+    for j in dkv_rows:
+        j = int(j)
+        dk_j, dv_j = np.zeros(d), np.zeros(d)
+        # queries that see key j: j itself and every real token below it
+        seers, frontier = [j], [j]
+        while frontier and j < tree.n_tokens:
+            frontier = [c for x in frontier for c in kids.get(x, ())]
+            seers.extend(frontier)
+        for i in seers:
+            for h in heads:
+                anc, p, ds, qi, doi = row_terms(i, h)
+                pos = int(np.nonzero(anc == j)[0][0])
+                dv_j += p[pos] * doi
+                dk_j += s * ds[pos] * qi
+        dkv[(j, g)] = (dk_j, dv_j)
+    return dq, dkv

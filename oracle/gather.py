@@ -1,0 +1,52 @@
+"""Oracle: per-sequence log-probabilities and entropies from packed-tree logits
+(test infrastructure only).
+
+The tree-training page (section "对数概率计算") explains why the labels cannot be
+obtained by rolling input_ids: positions are shared between sequences, so each
+sequence must recover its own token order from the tree.  The plain definition
+is used here: for every sequence s of length L and every position t, read the
+logits row of the tree token holding s[t] and take
+
+    logprob[t] = log_softmax(row)[s[t+1]]   for t < L-1,   logprob[L-1] = 0
+    entropy[t] = -sum_v p_v log p_v,        p = softmax(row)
+
+in float64, natural logs, temperature 1.  Outputs of the sequences of one tree
+are concatenated in ascending input index (the page's last step concatenates
+per-sequence results).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .tree import Tree
+
+
+def row_lse_entropy(rows: np.ndarray):
+    """log-sum-exp and entropy of each row of `rows` [n, V], in float64."""
+    x = np.asarray(rows, dtype=np.float64)
+    m = x.max(axis=1, keepdims=True)
+    e = np.exp(x - m)
+    z = e.sum(axis=1, keepdims=True)
+    lse = (m + np.log(z))[:, 0]
+    p = e / z
+    ent = lse - (p * x).sum(axis=1)
+    return lse, ent
+
+
+def gather_logprobs_entropy(tree: Tree, seqs, logits):
+    """logits: [Np, V] (any real dtype; only real rows are read).
+    Returns (logprobs, entropy), float64 arrays of length sum of the tree's
+    sequence lengths."""
+    outs_lp, outs_h = [], []
+    for sid in tree.seq_ids:
+        seq = np.asarray(seqs[sid])
+        idx = tree.seq_index[sid]
+        x = np.asarray(logits[idx], dtype=np.float64)
+        lse, ent = row_lse_entropy(x)
+        lp = np.zeros(len(seq))
+        nxt = seq[1:]
+        lp[:-1] = x[np.arange(len(seq) - 1), nxt] - lse[:-1]
+        outs_lp.append(lp)
+        outs_h.append(ent)
+    return np.concatenate(outs_lp), np.concatenate(outs_h)
