@@ -1,0 +1,225 @@
+"""Thin Python binding of libpst.  Torch supplies device memory and streams;
+every computation happens in the library.  Names follow the C ABI:
+
+    build_tree(seqs, max_tokens_per_mb)            -> Forest       (host)
+    tree_meta_create(forest, tree, stream=None)    -> TreeMeta     (device upload)
+    tree_attn_fwd(q, k, v, meta, ...)              -> (o, lse)
+    tree_attn_bwd(q, k, v, o, lse, dout, meta, ...) -> (dq, dk, dv)
+    gather_tree_logprobs_entropy(logits, meta, ...) -> (logprobs, entropy)
+"""
+
+from __future__ import annotations
+
+import ctypes
+from ctypes import byref, c_int32, c_size_t, c_void_p
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import _lib
+from ._lib import PST_BF16, PST_F32, PstError, check  # noqa: F401
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return PST_BF16
+    if t.dtype == torch.float32:
+        return PST_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _dev_tensor(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+class Forest:
+    """Sequences packed into compressed tries (host, library-owned)."""
+
+    def __init__(self, seqs: Sequence, max_tokens_per_mb: int):
+        lib = _lib.load()
+        arrs = [np.ascontiguousarray(s, dtype=np.int32).ravel() for s in seqs]
+        lens = np.array([a.size for a in arrs], dtype=np.int64)
+        self._tokens = np.concatenate(arrs) if arrs else np.zeros(0, np.int32)
+        self._offsets = np.zeros(len(arrs) + 1, dtype=np.int64)
+        np.cumsum(lens, out=self._offsets[1:])
+        self.n_seqs = len(arrs)
+        h = c_void_p()
+        self._h = None
+        check(lib.pst_build_tree(
+            self._tokens.ctypes.data_as(_lib.P32), self._offsets.ctypes.data_as(_lib.P64),
+            int(self.n_seqs), int(max_tokens_per_mb), byref(h)))
+        self._h = h
+        n = c_int32()
+        check(lib.pst_forest_num_trees(self._h, byref(n)))
+        self.n_trees = n.value
+
+    def close(self):
+        if self._h is not None:
+            _lib.load().pst_forest_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def sizes(self, tree: int) -> dict:
+        s = _lib.TreeSizes()
+        check(_lib.load().pst_forest_tree_sizes(self._h, int(tree), byref(s)))
+        return {f: getattr(s, f) for f, _ in s._fields_}
+
+    def stats(self) -> dict:
+        s = _lib.Stats()
+        check(_lib.load().pst_forest_stats(self._h, byref(s)))
+        return {f: getattr(s, f) for f, _ in s._fields_}
+
+    def seq_tree(self) -> np.ndarray:
+        out = np.zeros(self.n_seqs, dtype=np.int32)
+        check(_lib.load().pst_forest_seq_tree(self._h, out.ctypes.data_as(_lib.P32)))
+        return out
+
+    def export(self, tree: int) -> dict:
+        """Every array of tree `tree` as numpy (see pst_tree_arrays)."""
+        s = self.sizes(tree)
+        shapes = {
+            "token": s["n_padded"], "pos": s["n_padded"], "parent": s["n_padded"],
+            "subtree_end": s["n_padded"], "node": s["n_padded"],
+            "node_start": s["n_nodes"], "node_end": s["n_nodes"], "node_parent": s["n_nodes"],
+            "node_seq_ptr": s["n_nodes"] + 1, "node_seq_ids": s["n_node_seq"],
+            "seq_ids": s["n_seqs"], "seq_out_offsets": s["n_seqs"] + 1,
+            "seq_index": s["n_out"], "child_ptr": s["n_tokens"] + 1, "child_idx": s["n_edges"],
+            "q_ptr": s["n_blocks"] + 1, "q_kb": s["n_tiles"], "q_full": s["n_tiles"],
+            "kb_qhi": s["n_blocks"], "fwd_order": s["n_blocks"], "bwd_order": s["n_blocks"],
+        }
+        out, a = {}, _lib.TreeArrays()
+        for name in _lib.ARRAY_FIELDS:
+            dt = np.int64 if name == "seq_out_offsets" else np.int32
+            arr = np.zeros(max(shapes[name], 0), dtype=dt)
+            out[name] = arr
+            setattr(a, name, arr.ctypes.data_as(_lib.P64 if dt == np.int64 else _lib.P32))
+        check(_lib.load().pst_forest_export_tree(self._h, int(tree), byref(a)))
+        return out
+
+
+def build_tree(seqs: Sequence, max_tokens_per_mb: int) -> Forest:
+    return Forest(seqs, max_tokens_per_mb)
+
+
+class TreeMeta:
+    """Device-resident metadata of one tree (pst_tree_meta)."""
+
+    def __init__(self, forest: Forest, tree: int, stream=None):
+        h = c_void_p()
+        self._h = None
+        check(_lib.load().pst_tree_meta_create(forest._h, int(tree), c_void_p(_stream_ptr(stream)), byref(h)))
+        self._h = h
+        s = _lib.TreeSizes()
+        check(_lib.load().pst_tree_meta_sizes(self._h, byref(s)))
+        self.sizes = {f: getattr(s, f) for f, _ in s._fields_}
+        self.n_padded = self.sizes["n_padded"]
+        self.n_tokens = self.sizes["n_tokens"]
+        self.n_out = self.sizes["n_out"]
+
+    def destroy(self):
+        """Frees the device copy; the caller has synchronized every stream
+        that used it."""
+        if self._h is not None:
+            check(_lib.load().pst_tree_meta_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            if self._h is not None:
+                import torch
+                torch.cuda.synchronize()
+                self.destroy()
+        except Exception:
+            pass
+
+
+def tree_meta_create(forest: Forest, tree: int, stream=None) -> TreeMeta:
+    return TreeMeta(forest, tree, stream)
+
+
+def tree_attn_fwd(q, k, v, meta: TreeMeta, softmax_scale: Optional[float] = None,
+                  out=None, lse=None, stream=None):
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_tensor(t, n)
+    Np, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (Np, hkv, d) or v.shape != k.shape or Np != meta.n_padded:
+        raise ValueError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)} "
+                         f"do not match a tree of {meta.n_padded} padded rows")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, Np), dtype=torch.float32, device=q.device)
+    check(_lib.load().pst_tree_attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _dev_tensor(out, "out").data_ptr(),
+        _dev_tensor(lse, "lse").data_ptr(), meta._h, hq, hkv, d, _dtype_code(q),
+        float(softmax_scale or 0.0), c_void_p(_stream_ptr(stream))))
+    return out, lse
+
+
+def tree_attn_bwd_workspace_bytes(meta: TreeMeta, hq: int, head_dim: int) -> int:
+    n = c_size_t()
+    check(_lib.load().pst_tree_attn_bwd_workspace_bytes(meta._h, hq, head_dim, byref(n)))
+    return n.value
+
+
+def tree_attn_bwd(q, k, v, o, lse, dout, meta: TreeMeta, softmax_scale: Optional[float] = None,
+                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout")):
+        _dev_tensor(t, n)
+    Np, hq, d = q.shape
+    hkv = k.shape[1]
+    if (k.shape != (Np, hkv, d) or v.shape != k.shape or o.shape != q.shape
+            or dout.shape != q.shape or tuple(lse.shape) != (hq, Np) or Np != meta.n_padded):
+        raise ValueError("shape mismatch in tree_attn_bwd arguments")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nbytes = tree_attn_bwd_workspace_bytes(meta, hq, d)
+    if workspace is None:
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    check(_lib.load().pst_tree_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+        _dev_tensor(dq, "dq").data_ptr(), _dev_tensor(dk, "dk").data_ptr(),
+        _dev_tensor(dv, "dv").data_ptr(), _dev_tensor(workspace, "workspace").data_ptr(),
+        workspace.numel() * workspace.element_size(), meta._h, hq, hkv, d, _dtype_code(q),
+        float(softmax_scale or 0.0), c_void_p(_stream_ptr(stream))))
+    return dq, dk, dv
+
+
+def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=None, stream=None):
+    import torch
+    _dev_tensor(logits, "logits")
+    if logits.dim() != 2 or logits.shape[0] < meta.n_tokens:
+        raise ValueError(f"logits must be [>= {meta.n_tokens}, V], got {tuple(logits.shape)}")
+    n = meta.n_out
+    if logprobs is None:
+        logprobs = torch.empty(n, dtype=torch.float32, device=logits.device)
+    if entropy is None:
+        entropy = torch.empty(n, dtype=torch.float32, device=logits.device)
+    check(_lib.load().pst_gather_tree_logprobs_entropy(
+        logits.data_ptr(), int(logits.shape[1]), _dtype_code(logits), meta._h,
+        _dev_tensor(logprobs, "logprobs").data_ptr(), _dev_tensor(entropy, "entropy").data_ptr(),
+        c_void_p(_stream_ptr(stream))))
+    return logprobs, entropy

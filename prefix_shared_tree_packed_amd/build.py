@@ -1,0 +1,87 @@
+"""Builds libpst.so (the C ABI of include/pst.h) in-tree for gfx950.
+
+    python -m prefix_shared_tree_packed_amd.build
+
+Every HIP source is compiled with hipcc for --offload-arch=gfx950 with the
+packed-fp32 instructions disabled; the pure C++ host builder is compiled with
+g++; objects go to _build/ at the repository root and the library lands next
+to this file.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libpst.so")
+
+ARCH = "gfx950"
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+HIP_SOURCES = [
+    "capi.cpp",
+    "kernels/attn_fwd.hip",
+    "kernels/attn_bwd.hip",
+    "kernels/gather.hip",
+]
+CXX_SOURCES = ["host/forest.cpp"]
+
+
+def _hipcc() -> str:
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libpst.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    hipcc = _hipcc()
+    jobs = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
+        lang = ["-x", "hip"] if src.endswith(".cpp") else []
+        jobs.append([hipcc, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in CXX_SOURCES:
+        obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
+        jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs))
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,376 @@
+// The C ABI of libpst (declared in include/pst.h): argument checks, error
+// reporting, the host forest, the device metadata, and kernel dispatch.
+#include "pst.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "host/forest.h"
+#include "kernels/launch.h"
+
+struct pst_forest {
+  pst::Forest f;
+};
+
+// Device layout of one tree's metadata: a single int32 allocation holding
+// se [Np] | q_ptr [nb+1] | q_tile [n_tiles] | kb_qhi [nb] | fwd_order [nb] |
+// bwd_order [nb] | row_out_ptr [N+1] | out_pos [n_out] | out_tgt [n_out],
+// every section starting on a 16-byte boundary.  The pinned staging copy is
+// kept until destroy so the asynchronous upload never reads freed memory.
+struct pst_tree_meta {
+  int device = -1;
+  int32_t* dbuf = nullptr;
+  int32_t* hbuf = nullptr;
+  size_t n_words = 0;
+  pst_tree_sizes sizes{};
+  pst::TreeDev dev{};
+  int32_t min_target = 0;
+  int32_t max_target = -1;
+};
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const std::string& msg) {
+  g_error = msg;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return PST_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PST_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+void fill_sizes(const pst::Tree& t, pst_tree_sizes* s) {
+  s->n_tokens = t.N;
+  s->n_padded = t.Np;
+  s->n_blocks = t.nb;
+  s->n_nodes = static_cast<int32_t>(t.node_start.size());
+  s->n_seqs = static_cast<int32_t>(t.seq_ids.size());
+  s->n_edges = static_cast<int32_t>(t.child_idx.size());
+  s->n_tiles = t.n_tiles();
+  s->n_node_seq = static_cast<int32_t>(t.node_seq_ids.size());
+  s->n_out = t.n_out();
+  s->n_pairs = t.n_pairs;
+}
+
+template <typename A, typename B>
+void copy_out(B* dst, const std::vector<A>& src) {
+  if (dst && !src.empty()) std::memcpy(dst, src.data(), src.size() * sizeof(A));
+}
+
+int check_tree(const pst_forest* forest, int32_t tree) {
+  if (!forest) return fail(PST_EINVAL, "forest is NULL");
+  if (tree < 0 || tree >= static_cast<int32_t>(forest->f.trees.size()))
+    return fail(PST_ERANGE, "tree index " + std::to_string(tree) + " out of range [0, " +
+                                std::to_string(forest->f.trees.size()) + ")");
+  return PST_OK;
+}
+
+int check_meta_device(const pst_tree_meta* meta) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != meta->device)
+    return fail(PST_EINVAL, "tree metadata lives on device " + std::to_string(meta->device) +
+                                " but the current device is " + std::to_string(dev));
+  return PST_OK;
+}
+
+int check_attn_args(const pst_tree_meta* meta, int32_t hq, int32_t hkv, int32_t head_dim,
+                    int32_t dtype) {
+  if (!meta) return fail(PST_EINVAL, "tree metadata is NULL");
+  if (dtype != PST_F32 && dtype != PST_BF16)
+    return fail(PST_EDTYPE, "unknown dtype " + std::to_string(dtype));
+  if (hq <= 0 || hkv <= 0) return fail(PST_ESHAPE, "head counts must be positive");
+  if (hq % hkv)
+    return fail(PST_ESHAPE, "hq=" + std::to_string(hq) + " is not a multiple of hkv=" +
+                                std::to_string(hkv));
+  if (dtype == PST_BF16 && head_dim != 64 && head_dim != 128)
+    return fail(PST_ESHAPE, "bf16 head_dim must be 64 or 128, got " + std::to_string(head_dim));
+  if (dtype == PST_F32 && head_dim != 64)
+    return fail(PST_ESHAPE, "fp32 head_dim must be 64, got " + std::to_string(head_dim));
+  if (static_cast<int64_t>(meta->sizes.n_padded) * hq >= (int64_t{1} << 31))
+    return fail(PST_ESHAPE, "Np * hq exceeds 2^31");
+  return PST_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps, const char* names) {
+  for (const void* p : ps) {
+    if (!p) return fail(PST_EINVAL, std::string("NULL device pointer among ") + names);
+    if (!aligned16(p)) return fail(PST_ESHAPE, std::string("device pointer not 16-byte aligned among ") + names);
+  }
+  return PST_OK;
+}
+
+float resolve_scale(float s, int32_t head_dim) {
+  return s > 0.f ? s : 1.0f / std::sqrt(static_cast<float>(head_dim));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pst_last_error(void) { return g_error.c_str(); }
+
+int pst_build_tree(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
+                   int32_t max_tokens_per_mb, pst_forest** out) {
+  if (!out) return fail(PST_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!seq_offsets) return fail(PST_EINVAL, "seq_offsets is NULL");
+  if (n_seqs >= 1 && !tokens) return fail(PST_EINVAL, "tokens is NULL");
+  pst_forest* f = new (std::nothrow) pst_forest;
+  if (!f) return fail(PST_ENOMEM, "out of host memory");
+  std::string err;
+  int st;
+  try {
+    st = pst::build_forest(tokens, seq_offsets, n_seqs, max_tokens_per_mb, f->f, err);
+  } catch (const std::bad_alloc&) {
+    delete f;
+    return fail(PST_ENOMEM, "out of host memory while packing");
+  }
+  if (st != pst::kBuildOk) {
+    delete f;
+    const int code = st == pst::kBuildCapacity ? PST_ECAPACITY
+                     : st == pst::kBuildBlock  ? PST_EBLOCK
+                                               : PST_EINVAL;
+    return fail(code, err);
+  }
+  *out = f;
+  return ok();
+}
+
+int pst_forest_num_trees(const pst_forest* forest, int32_t* n_trees) {
+  if (!forest || !n_trees) return fail(PST_EINVAL, "NULL argument");
+  *n_trees = static_cast<int32_t>(forest->f.trees.size());
+  return ok();
+}
+
+int pst_forest_tree_sizes(const pst_forest* forest, int32_t tree, pst_tree_sizes* out) {
+  if (int e = check_tree(forest, tree)) return e;
+  if (!out) return fail(PST_EINVAL, "out is NULL");
+  fill_sizes(forest->f.trees[tree], out);
+  return ok();
+}
+
+int pst_forest_export_tree(const pst_forest* forest, int32_t tree, const pst_tree_arrays* a) {
+  if (int e = check_tree(forest, tree)) return e;
+  if (!a) return fail(PST_EINVAL, "arrays is NULL");
+  const pst::Tree& t = forest->f.trees[tree];
+  copy_out(a->token, t.token);
+  copy_out(a->pos, t.pos);
+  copy_out(a->parent, t.parent);
+  copy_out(a->subtree_end, t.se);
+  copy_out(a->node, t.node);
+  copy_out(a->node_start, t.node_start);
+  copy_out(a->node_end, t.node_end);
+  copy_out(a->node_parent, t.node_parent);
+  copy_out(a->node_seq_ptr, t.node_seq_ptr);
+  copy_out(a->node_seq_ids, t.node_seq_ids);
+  copy_out(a->seq_ids, t.seq_ids);
+  copy_out(a->seq_out_offsets, t.seq_out_offsets);
+  copy_out(a->seq_index, t.seq_index);
+  copy_out(a->child_ptr, t.child_ptr);
+  copy_out(a->child_idx, t.child_idx);
+  copy_out(a->q_ptr, t.q_ptr);
+  copy_out(a->q_kb, t.q_kb);
+  copy_out(a->q_full, t.q_full);
+  copy_out(a->kb_qhi, t.kb_qhi);
+  copy_out(a->fwd_order, t.fwd_order);
+  copy_out(a->bwd_order, t.bwd_order);
+  return ok();
+}
+
+int pst_forest_seq_tree(const pst_forest* forest, int32_t* tree_of_seq) {
+  if (!forest || !tree_of_seq) return fail(PST_EINVAL, "NULL argument");
+  copy_out(tree_of_seq, forest->f.seq_tree);
+  return ok();
+}
+
+int pst_forest_stats(const pst_forest* forest, pst_stats* out) {
+  if (!forest || !out) return fail(PST_EINVAL, "NULL argument");
+  const pst::Forest& f = forest->f;
+  pst_stats s{};
+  s.n_trees = static_cast<int32_t>(f.trees.size());
+  s.n_seqs = f.n_seqs;
+  s.orig_tokens = f.orig_tokens;
+  s.causal_pairs = f.causal_pairs;
+  for (const pst::Tree& t : f.trees) {
+    s.tree_tokens += t.N;
+    s.padded_tokens += t.Np;
+    s.n_pairs += t.n_pairs;
+    s.n_tiles += t.n_tiles();
+  }
+  s.tree_token_ratio = static_cast<double>(s.tree_tokens) / static_cast<double>(s.orig_tokens);
+  *out = s;
+  return ok();
+}
+
+void pst_forest_free(pst_forest* forest) { delete forest; }
+
+int pst_tree_meta_create(const pst_forest* forest, int32_t tree, void* stream,
+                         pst_tree_meta** out) {
+  if (!out) return fail(PST_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (int e = check_tree(forest, tree)) return e;
+  const pst::Tree& t = forest->f.trees[tree];
+
+  auto round4 = [](size_t n) { return (n + 3) / 4 * 4; };
+  const size_t n_tiles = t.q_kb.size();
+  const size_t n_out = static_cast<size_t>(t.n_out());
+  size_t off = 0;
+  const size_t o_se = off;        off += round4(t.Np);
+  const size_t o_qptr = off;      off += round4(t.nb + 1);
+  const size_t o_qtile = off;     off += round4(n_tiles);
+  const size_t o_qhi = off;       off += round4(t.nb);
+  const size_t o_ford = off;      off += round4(t.nb);
+  const size_t o_bord = off;      off += round4(t.nb);
+  const size_t o_rptr = off;      off += round4(static_cast<size_t>(t.N) + 1);
+  const size_t o_opos = off;      off += round4(n_out);
+  const size_t o_otgt = off;      off += round4(n_out);
+  const size_t words = off;
+
+  pst_tree_meta* m = new (std::nothrow) pst_tree_meta;
+  if (!m) return fail(PST_ENOMEM, "out of host memory");
+  hipError_t e = hipGetDevice(&m->device);
+  if (e != hipSuccess) {
+    delete m;
+    return hip_fail(e, "hipGetDevice");
+  }
+  e = hipHostMalloc(reinterpret_cast<void**>(&m->hbuf), words * sizeof(int32_t), hipHostMallocDefault);
+  if (e != hipSuccess) {
+    delete m;
+    return fail(PST_ENOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  }
+  e = hipMalloc(reinterpret_cast<void**>(&m->dbuf), words * sizeof(int32_t));
+  if (e != hipSuccess) {
+    (void)hipHostFree(m->hbuf);
+    delete m;
+    return fail(PST_ENOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+  }
+  int32_t* h = m->hbuf;
+  std::memset(h, 0, words * sizeof(int32_t));
+  std::memcpy(h + o_se, t.se.data(), t.se.size() * 4);
+  std::memcpy(h + o_qptr, t.q_ptr.data(), t.q_ptr.size() * 4);
+  for (size_t i = 0; i < n_tiles; ++i) h[o_qtile + i] = (t.q_kb[i] << 1) | (t.q_full[i] & 1);
+  std::memcpy(h + o_qhi, t.kb_qhi.data(), t.kb_qhi.size() * 4);
+  std::memcpy(h + o_ford, t.fwd_order.data(), t.fwd_order.size() * 4);
+  std::memcpy(h + o_bord, t.bwd_order.data(), t.bwd_order.size() * 4);
+  std::memcpy(h + o_rptr, t.row_out_ptr.data(), t.row_out_ptr.size() * 4);
+  if (n_out) {
+    std::memcpy(h + o_opos, t.out_pos.data(), n_out * 4);
+    std::memcpy(h + o_otgt, t.out_tgt.data(), n_out * 4);
+  }
+  e = hipMemcpyAsync(m->dbuf, h, words * sizeof(int32_t), hipMemcpyHostToDevice,
+                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipFree(m->dbuf);
+    (void)hipHostFree(m->hbuf);
+    delete m;
+    return hip_fail(e, "hipMemcpyAsync");
+  }
+  m->n_words = words;
+  fill_sizes(t, &m->sizes);
+  int32_t* d = m->dbuf;
+  m->dev = pst::TreeDev{d + o_se,   d + o_qptr, d + o_qtile, d + o_qhi,  d + o_ford,
+                        d + o_bord, d + o_rptr, d + o_opos,  d + o_otgt, t.N,
+                        t.Np,       t.nb,       static_cast<int32_t>(n_tiles)};
+  m->min_target = t.min_target;
+  m->max_target = t.max_target;
+  *out = m;
+  return ok();
+}
+
+int pst_tree_meta_sizes(const pst_tree_meta* meta, pst_tree_sizes* out) {
+  if (!meta || !out) return fail(PST_EINVAL, "NULL argument");
+  *out = meta->sizes;
+  return ok();
+}
+
+int pst_tree_meta_destroy(pst_tree_meta* meta) {
+  if (!meta) return ok();
+  hipError_t e1 = hipFree(meta->dbuf);
+  hipError_t e2 = hipHostFree(meta->hbuf);
+  delete meta;
+  if (e1 != hipSuccess) return hip_fail(e1, "hipFree");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipHostFree");
+  return ok();
+}
+
+int pst_tree_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const pst_tree_meta* meta, int32_t hq, int32_t hkv, int32_t head_dim,
+                      int32_t dtype, float softmax_scale, void* stream) {
+  if (int e = check_attn_args(meta, hq, hkv, head_dim, dtype)) return e;
+  if (int e = check_ptrs({q, k, v, o, lse}, "q, k, v, o, lse")) return e;
+  if (int e = check_meta_device(meta)) return e;
+  const hipError_t e = pst::launch_attn_fwd(dtype, head_dim, q, k, v, o, lse, meta->dev, hq, hkv,
+                                            resolve_scale(softmax_scale, head_dim),
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tree_attn_fwd launch");
+  return ok();
+}
+
+int pst_tree_attn_bwd_workspace_bytes(const pst_tree_meta* meta, int32_t hq, int32_t head_dim,
+                                      size_t* bytes) {
+  (void)head_dim;
+  if (!meta || !bytes) return fail(PST_EINVAL, "NULL argument");
+  if (hq <= 0) return fail(PST_ESHAPE, "hq must be positive");
+  *bytes = static_cast<size_t>(meta->sizes.n_padded) * hq * sizeof(float);
+  return ok();
+}
+
+int pst_tree_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, const pst_tree_meta* meta,
+                      int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
+                      float softmax_scale, void* stream) {
+  if (int e = check_attn_args(meta, hq, hkv, head_dim, dtype)) return e;
+  if (int e = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv, workspace},
+                         "q, k, v, o, lse, dout, dq, dk, dv, workspace"))
+    return e;
+  const size_t need = static_cast<size_t>(meta->sizes.n_padded) * hq * sizeof(float);
+  if (workspace_bytes < need)
+    return fail(PST_EINVAL, "workspace of " + std::to_string(workspace_bytes) + " bytes < " +
+                                std::to_string(need) + " needed");
+  if (int e = check_meta_device(meta)) return e;
+  const hipError_t e = pst::launch_attn_bwd(
+      dtype, head_dim, q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
+      meta->dev, hq, hkv, resolve_scale(softmax_scale, head_dim), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tree_attn_bwd launch");
+  return ok();
+}
+
+int pst_gather_tree_logprobs_entropy(const void* logits, int64_t vocab, int32_t dtype,
+                                     const pst_tree_meta* meta, float* logprobs,
+                                     float* entropy, void* stream) {
+  if (!meta) return fail(PST_EINVAL, "tree metadata is NULL");
+  if (dtype != PST_F32 && dtype != PST_BF16)
+    return fail(PST_EDTYPE, "unknown dtype " + std::to_string(dtype));
+  if (vocab <= 0) return fail(PST_EINVAL, "vocab must be positive");
+  if (meta->max_target >= vocab || meta->min_target < 0)
+    return fail(PST_EINVAL, "next-token ids span [" + std::to_string(meta->min_target) + ", " +
+                                std::to_string(meta->max_target) + "], outside the vocab of " +
+                                std::to_string(vocab));
+  if (!logits || !logprobs || !entropy) return fail(PST_EINVAL, "NULL device pointer");
+  const size_t esz = dtype == PST_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(logits) % esz)
+    return fail(PST_ESHAPE, "logits pointer is not aligned to its element size");
+  if (int e = check_meta_device(meta)) return e;
+  const hipError_t e = pst::launch_gather(dtype, logits, vocab, meta->dev, logprobs, entropy,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+}  // extern "C"

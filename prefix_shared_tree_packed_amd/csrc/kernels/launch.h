@@ -1,0 +1,31 @@
+// Host-side launchers of the gfx950 kernels.  Shapes and pointers are
+// validated by the C ABI layer before any of these is called; each launcher
+// enqueues its kernels on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "common.h"
+
+namespace pst {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBf16 = 1;
+
+hipError_t launch_attn_fwd(int dtype, int head_dim, const void* q, const void* k, const void* v,
+                           void* o, float* lse, const TreeDev& tr, int hq, int hkv, float scale,
+                           hipStream_t stream);
+
+// workspace: float32 [hq, Np] (the per-row dO.O sums).
+hipError_t launch_attn_bwd(int dtype, int head_dim, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                           void* dv, float* workspace, const TreeDev& tr, int hq, int hkv,
+                           float scale, hipStream_t stream);
+
+hipError_t launch_gather(int dtype, const void* logits, int64_t vocab, const TreeDev& tr,
+                         float* logprobs, float* entropy, hipStream_t stream);
+
+}  // namespace pst

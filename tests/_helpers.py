@@ -1,0 +1,93 @@
+"""Shared helpers of the GPU parity tests: build a case with both the library
+and the oracle, draw seeded inputs on the device, compare with tolerances.
+
+Tolerances (float outputs; integer outputs are compared bit-exactly):
+  fp32 attention:  |got - ref| <= 1e-5 |ref| + 1e-6
+  bf16 attention:  |got - ref| <= 2e-2 (O, LSE, dQ, dK, dV)
+  logprob/entropy: |got - ref| <= 1e-3 from bf16 logits, 1e-5 |ref| + 1e-6 from fp32
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import prefix_shared_tree_packed_amd as pst
+from workloads import make_tensor, tree_tensor_seed
+
+
+def tol(dtype):
+    return (1e-5, 1e-6) if dtype == "f32" else (0.0, 2e-2)
+
+
+def assert_close(got, ref, dtype, what, rtol=None, atol=None):
+    r, a = tol(dtype)
+    r = r if rtol is None else rtol
+    a = a if atol is None else atol
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    bound = a + r * np.abs(ref)
+    bad = err > bound
+    if bad.any():
+        idx = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())}/{err.size} out of tolerance; worst at {idx}: "
+            f"got {got[idx]!r} ref {ref[idx]!r} (max abs err {err.max():.3g})")
+
+
+def torch_dtype(dtype):
+    import torch
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+def host(t):
+    import torch
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def host32(t):
+    """float32 host copy (exact for bf16 and fp32 values; half the memory of
+    float64 for the full-size sampled checks)."""
+    import torch
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def attn_inputs(Np, hq, hkv, d, dtype, seed, device="cuda", with_dout=False):
+    q = make_tensor((Np, hq, d), dtype, tree_tensor_seed(seed, 0, "q"), device)
+    k = make_tensor((Np, hkv, d), dtype, tree_tensor_seed(seed, 0, "k"), device)
+    v = make_tensor((Np, hkv, d), dtype, tree_tensor_seed(seed, 0, "v"), device)
+    if not with_dout:
+        return q, k, v
+    do = make_tensor((Np, hq, d), dtype, tree_tensor_seed(seed, 0, "do"), device)
+    return q, k, v, do
+
+
+class Case:
+    """One forest built twice: by the library (device metadata) and by the oracle."""
+
+    def __init__(self, seqs, cap):
+        self.seqs = seqs
+        self.forest = pst.build_tree(seqs, cap)
+        self.ref = oracle.build_forest(seqs, cap)
+        assert self.forest.n_trees == len(self.ref.trees)
+        self.metas = [pst.tree_meta_create(self.forest, t) for t in range(self.forest.n_trees)]
+
+    def close(self):
+        import torch
+        torch.cuda.synchronize()
+        for m in self.metas:
+            m.destroy()
+        self.forest.close()
+
+
+def prompt_groups(rng, n_prompts, prompt_len, n_resp, resp_lo, resp_hi, vocab=1000):
+    seqs = []
+    for p in range(n_prompts):
+        prompt = rng.integers(0, vocab, size=prompt_len)
+        prompt[0] = p  # distinct roots
+        for r in range(n_resp):
+            resp = rng.integers(0, vocab, size=int(rng.integers(resp_lo, resp_hi + 1)))
+            resp[0] = r  # distinct forks
+            seqs.append(np.concatenate([prompt, resp]).astype(np.int32))
+    return seqs

@@ -1,0 +1,52 @@
+"""The C ABI library loads, exports every function include/pst.h declares,
+and rejects bad arguments before any HIP call (CPU only: no call here
+reaches the GPU)."""
+
+import ctypes
+
+import pytest
+
+import prefix_shared_tree_packed_amd as pst
+from prefix_shared_tree_packed_amd import _lib
+
+
+def test_exports_every_declared_function():
+    lib = pst.load()
+    names = pst.header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib._SIGS), "binding and header disagree"
+
+
+def test_device_entry_points_reject_null_meta():
+    lib = pst.load()
+    p = ctypes.c_void_p(16)
+    rc = lib.pst_tree_attn_fwd(p, p, p, p, p, None, 32, 8, 128, 1, 0.0, None)
+    assert _lib.ERRORS[rc] == "PST_EINVAL"
+    rc = lib.pst_gather_tree_logprobs_entropy(p, 100, 1, None, p, p, None)
+    assert _lib.ERRORS[rc] == "PST_EINVAL"
+    rc = lib.pst_tree_attn_bwd(p, p, p, p, p, p, p, p, p, p, 0, None, 32, 8, 128, 1, 0.0, None)
+    assert _lib.ERRORS[rc] == "PST_EINVAL"
+    assert b"NULL" in lib.pst_last_error()
+
+
+def test_meta_create_rejects_bad_tree_index():
+    f = pst.build_tree([[1, 2, 3]], 128)
+    lib = pst.load()
+    out = ctypes.c_void_p()
+    for t in (-1, 1):
+        rc = lib.pst_tree_meta_create(f._h, t, None, ctypes.byref(out))
+        assert _lib.ERRORS[rc] == "PST_ERANGE"
+        assert not out.value
+
+
+def test_null_arguments():
+    lib = pst.load()
+    out = ctypes.c_void_p()
+    assert _lib.ERRORS[lib.pst_build_tree(None, None, 1, 128, ctypes.byref(out))] == "PST_EINVAL"
+    assert _lib.ERRORS[lib.pst_forest_num_trees(None, None)] == "PST_EINVAL"
+    assert _lib.ERRORS[lib.pst_forest_stats(None, None)] == "PST_EINVAL"
+    f = pst.build_tree([[1, 2, 3]], 128)
+    with pytest.raises(pst.PstError):
+        f.sizes(5)

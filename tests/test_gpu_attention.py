@@ -1,0 +1,214 @@
+"""Tree attention forward/backward on the GPU against the oracle (through the
+C ABI).  Small cases are compared element by element over every output;
+full-size workloads on sampled rows that the oracle evaluates one by one."""
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import get_workload, worked_example, worked_example_edge
+
+from _helpers import Case, assert_close, attn_inputs, host, host32, prompt_groups
+
+pytestmark = pytest.mark.gpu
+
+
+def _fwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, seed, scale=None):
+    case = Case(seqs, cap)
+    try:
+        for t, tree in enumerate(case.ref.trees):
+            print(f"fwd case: dtype={dtype} hq={hq} hkv={hkv} d={d} tree={t} Np={tree.n_padded}", flush=True)
+            q, k, v = attn_inputs(tree.n_padded, hq, hkv, d, dtype, seed + t)
+            o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[t], softmax_scale=scale)
+            O, LSE = oracle.attn_fwd(tree, host(q), host(k), host(v), scale=scale)
+            assert_close(host(o), O, dtype, "O")
+            assert_close(host(lse), LSE, dtype, "LSE")
+    finally:
+        case.close()
+
+
+def test_fwd_worked_example_fp32(gpu_lib):
+    _fwd_full(gpu_lib, worked_example(), 128, 2, 1, 64, "f32", 1)
+    _fwd_full(gpu_lib, worked_example_edge(), 128, 2, 2, 64, "f32", 2)
+
+
+def test_fwd_worked_example_bf16(gpu_lib):
+    _fwd_full(gpu_lib, worked_example(), 128, 4, 1, 128, "bf16", 3)
+    _fwd_full(gpu_lib, worked_example(), 128, 2, 2, 64, "bf16", 4, scale=0.2)
+
+
+def test_fwd_tiny_workload(gpu_lib):
+    w = get_workload("tiny")
+    _fwd_full(gpu_lib, w.seqs, w.max_tokens_per_mb, w.hq, w.hkv, w.head_dim, w.dtype, w.seed)
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("f32", 4, 2, 64), ("bf16", 8, 2, 128),
+                                             ("bf16", 5, 1, 64), ("bf16", 6, 6, 128)])
+def test_fwd_several_tiles(gpu_lib, dtype, hq, hkv, d):
+    """Trees spanning several 128-blocks with a ragged tail, several trees."""
+    rng = np.random.default_rng(hq * 7 + d)
+    seqs = prompt_groups(rng, 3, 150, 3, 20, 260)
+    _fwd_full(gpu_lib, seqs, 1024, hq, hkv, d, dtype, 10 + hq)
+
+
+def test_fwd_no_sharing(gpu_lib):
+    """Distinct sequences: every tree token sees exactly its causal prefix."""
+    rng = np.random.default_rng(5)
+    seqs = [np.concatenate([[i], rng.integers(0, 50, size=int(rng.integers(100, 400)))]).astype(np.int32)
+            for i in range(5)]
+    _fwd_full(gpu_lib, seqs, 1024, 8, 2, 128, "bf16", 21)
+
+
+def test_fwd_single_long_chain(gpu_lib):
+    """One sequence filling its tree exactly: plain causal attention, every
+    off-diagonal tile full."""
+    seqs = [np.arange(1, 641, dtype=np.int32)]
+    _fwd_full(gpu_lib, seqs, 640, 4, 4, 64, "f32", 22)
+    _fwd_full(gpu_lib, seqs, 640, 8, 2, 128, "bf16", 23)
+
+
+def _fwd_sampled(gpu_lib, name, n_rows=48, n_trees=None):
+    w = get_workload(name)
+    case = Case(w.seqs, w.max_tokens_per_mb)
+    rng = np.random.default_rng(0)
+    try:
+        trees = range(len(case.ref.trees)) if n_trees is None else range(min(n_trees, len(case.ref.trees)))
+        for t in trees:
+            tree = case.ref.trees[t]
+            print(f"fwd sampled: {name} tree={t} Np={tree.n_padded}", flush=True)
+            q, k, v = attn_inputs(tree.n_padded, w.hq, w.hkv, w.head_dim, w.dtype, w.seed * 100 + t)
+            o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[t])
+            rows = sorted(set(rng.integers(0, tree.n_padded, size=n_rows).tolist())
+                          | {0, tree.n_tokens - 1, tree.n_padded - 1})
+            heads = sorted(set(rng.integers(0, w.hq, size=6).tolist()) | {0, w.hq - 1})
+            qh, kh, vh = host32(q), host32(k), host32(v)
+            ref = oracle.attn_fwd_rows(tree, qh, kh, vh, rows, heads)
+            oh, lh = host32(o), host32(lse)
+            got = np.array([oh[i, h] for (i, h) in ref])
+            exp = np.array([x[0] for x in ref.values()])
+            assert_close(got, exp, w.dtype, f"O[{name}]")
+            assert_close(np.array([lh[h, i] for (i, h) in ref]),
+                         np.array([x[1] for x in ref.values()]), w.dtype, f"LSE[{name}]")
+    finally:
+        case.close()
+
+
+def test_fwd_grpo_sampled(gpu_lib):
+    _fwd_sampled(gpu_lib, "grpo")
+
+
+def test_fwd_bimodal_sampled(gpu_lib):
+    _fwd_sampled(gpu_lib, "bimodal", n_trees=3)
+
+
+def test_fwd_long_sampled(gpu_lib):
+    _fwd_sampled(gpu_lib, "long", n_rows=24)
+
+
+def test_fwd_long_control_sampled(gpu_lib):
+    _fwd_sampled(gpu_lib, "long_control", n_rows=16, n_trees=2)
+
+
+# ---------------------------------------------------------------- backward
+
+def _bwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, seed):
+    case = Case(seqs, cap)
+    try:
+        for t, tree in enumerate(case.ref.trees):
+            print(f"bwd case: dtype={dtype} hq={hq} hkv={hkv} d={d} tree={t} Np={tree.n_padded}", flush=True)
+            q, k, v, do = attn_inputs(tree.n_padded, hq, hkv, d, dtype, seed + t, with_dout=True)
+            o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[t])
+            dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[t])
+            rdq, rdk, rdv = oracle.attn_bwd(tree, host(q), host(k), host(v), host(do))
+            assert_close(host(dq), rdq, dtype, "dQ")
+            assert_close(host(dk), rdk, dtype, "dK")
+            assert_close(host(dv), rdv, dtype, "dV")
+    finally:
+        case.close()
+
+
+def test_bwd_worked_example(gpu_lib):
+    _bwd_full(gpu_lib, worked_example_edge(), 128, 2, 1, 64, "f32", 31)
+    _bwd_full(gpu_lib, worked_example(), 128, 4, 2, 128, "bf16", 32)
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("f32", 4, 2, 64), ("bf16", 8, 2, 128),
+                                             ("bf16", 5, 1, 64)])
+def test_bwd_several_tiles(gpu_lib, dtype, hq, hkv, d):
+    rng = np.random.default_rng(hq * 13 + d)
+    seqs = prompt_groups(rng, 3, 150, 3, 20, 260)
+    _bwd_full(gpu_lib, seqs, 1024, hq, hkv, d, dtype, 40 + hq)
+
+
+def test_bwd_single_long_chain(gpu_lib):
+    _bwd_full(gpu_lib, [np.arange(1, 513, dtype=np.int32)], 512, 8, 2, 128, "bf16", 45)
+
+
+def test_bwd_deterministic(gpu_lib):
+    import torch
+    rng = np.random.default_rng(9)
+    seqs = prompt_groups(rng, 2, 200, 4, 50, 300)
+    case = Case(seqs, 2048)
+    try:
+        tree = case.ref.trees[0]
+        q, k, v, do = attn_inputs(tree.n_padded, 8, 2, 128, "bf16", 50, with_dout=True)
+        o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[0])
+        a = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[0])
+        b = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[0])
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    finally:
+        case.close()
+
+
+def test_bwd_agentic_sampled(gpu_lib):
+    """Full-size agentic trees: dQ on sampled rows, dK/dV on sampled deep keys
+    (whose visible queries the oracle can enumerate one by one)."""
+    w = get_workload("agentic")
+    case = Case(w.seqs, w.max_tokens_per_mb)
+    rng = np.random.default_rng(1)
+    try:
+        for t, tree in enumerate(case.ref.trees):
+            print(f"bwd sampled: agentic tree={t} Np={tree.n_padded}", flush=True)
+            q, k, v, do = attn_inputs(tree.n_padded, w.hq, w.hkv, w.head_dim, w.dtype,
+                                      w.seed * 100 + t, with_dout=True)
+            o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[t])
+            dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[t])
+            qh, kh, vh, doh = host32(q), host32(k), host32(v), host32(do)
+            dqh, dkh, dvh = host32(dq), host32(dk), host32(dv)
+            se = tree.subtree_end
+            deep = [j for j in range(tree.n_tokens) if se[j] - j < 40]
+            keys = sorted(rng.choice(deep, size=8, replace=False).tolist()) + [tree.n_padded - 1]
+            rows = sorted(rng.integers(0, tree.n_tokens, size=8).tolist())
+            for g in (0, w.hkv - 1):
+                G = w.hq // w.hkv
+                heads = list(range(g * G, (g + 1) * G))
+                rq, rkv = oracle.attn_bwd_rows(tree, qh, kh, vh, doh, rows, keys, (g, heads))
+                assert_close(np.array([dqh[i, h] for (i, h) in rq]), np.array(list(rq.values())),
+                             w.dtype, "dQ[agentic]")
+                assert_close(np.array([dkh[j, gg] for (j, gg) in rkv]),
+                             np.array([x[0] for x in rkv.values()]), w.dtype, "dK[agentic]")
+                assert_close(np.array([dvh[j, gg] for (j, gg) in rkv]),
+                             np.array([x[1] for x in rkv.values()]), w.dtype, "dV[agentic]")
+    finally:
+        case.close()
+
+
+def test_invalid_shapes_rejected(gpu_lib):
+    import torch
+    case = Case(worked_example(), 128)
+    try:
+        q, k, v = attn_inputs(128, 6, 4, 128, "bf16", 1)
+        with pytest.raises(gpu_lib.PstError) as e:
+            gpu_lib.tree_attn_fwd(q, k, v, case.metas[0])
+        assert e.value.name == "PST_ESHAPE"
+        q, k, v = attn_inputs(128, 4, 2, 96, "bf16", 1)
+        with pytest.raises(gpu_lib.PstError):
+            gpu_lib.tree_attn_fwd(q, k, v, case.metas[0])
+        q, k, v = attn_inputs(128, 4, 2, 64, "bf16", 1)
+        with pytest.raises(TypeError):
+            gpu_lib.tree_attn_fwd(q.half(), k.half(), v.half(), case.metas[0])
+        torch.cuda.synchronize()
+    finally:
+        case.close()

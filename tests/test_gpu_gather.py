@@ -1,0 +1,103 @@
+"""Logprob/entropy gather on the GPU against the oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import get_workload, make_tensor, tree_tensor_seed, worked_example, worked_example_edge
+
+from _helpers import Case, assert_close, host, prompt_groups
+
+pytestmark = pytest.mark.gpu
+
+
+def _tol(dtype):
+    return dict(rtol=0.0, atol=1e-3) if dtype == "bf16" else dict(rtol=1e-5, atol=1e-6)
+
+
+def _run(gpu_lib, seqs, cap, vocab, dtype, seed, std=1.0, seq_sample=None):
+    case = Case(seqs, cap)
+    rng = np.random.default_rng(seed)
+    try:
+        for t, tree in enumerate(case.ref.trees):
+            print(f"gather case: dtype={dtype} V={vocab} tree={t} N={tree.n_tokens}", flush=True)
+            logits = make_tensor((tree.n_padded, vocab), dtype, tree_tensor_seed(seed, t, "logits"),
+                                 "cuda", std=std)
+            lp, ent = gpu_lib.gather_tree_logprobs_entropy(logits, case.metas[t])
+            lph, enth = host(lp), host(ent)
+            ids = tree.seq_ids
+            if seq_sample is not None and len(ids) > seq_sample:
+                ids = sorted(rng.choice(ids, size=seq_sample, replace=False).tolist())
+            lg = host(logits[:tree.n_tokens])
+            for sid in ids:
+                k = tree.seq_ids.index(sid)
+                a, b = tree.out_offsets[k], tree.out_offsets[k + 1]
+                sub = oracle.Tree(**{**tree.__dict__, "seq_ids": [sid],
+                                     "out_offsets": np.array([0, b - a])})
+                rlp, rent = oracle.gather_logprobs_entropy(sub, seqs, lg)
+                assert_close(lph[a:b], rlp, dtype, f"logprob seq {sid}", **_tol(dtype))
+                assert_close(enth[a:b], rent, dtype, f"entropy seq {sid}", **_tol(dtype))
+    finally:
+        case.close()
+
+
+def test_gather_worked_example(gpu_lib):
+    _run(gpu_lib, worked_example(), 128, 9, "f32", 1)       # 36-byte rows: unaligned
+    _run(gpu_lib, worked_example_edge(), 128, 64, "bf16", 2, std=2.0)
+
+
+def test_gather_tiny_workload(gpu_lib):
+    w = get_workload("tiny")
+    _run(gpu_lib, w.seqs, w.max_tokens_per_mb, w.vocab, w.dtype, w.seed, std=w.logit_std)
+
+
+@pytest.mark.parametrize("vocab,dtype", [(1001, "bf16"), (4099, "f32"), (32000, "bf16")])
+def test_gather_several_trees(gpu_lib, vocab, dtype):
+    rng = np.random.default_rng(vocab)
+    seqs = prompt_groups(rng, 4, 100, 4, 10, 200, vocab=min(vocab, 1000))
+    _run(gpu_lib, seqs, 512, vocab, dtype, vocab, std=2.0)
+
+
+def test_gather_closed_forms(gpu_lib):
+    """Uniform logits: logprob = -log V, entropy = log V (0 on last tokens)."""
+    import torch
+    seqs = worked_example_edge()
+    case = Case(seqs, 128)
+    try:
+        V = 32000
+        logits = torch.full((128, V), 0.5, dtype=torch.bfloat16, device="cuda")
+        lp, ent = gpu_lib.gather_tree_logprobs_entropy(logits, case.metas[0])
+        lph, enth = host(lp), host(ent)
+        last = set((case.ref.trees[0].out_offsets[1:] - 1).tolist())
+        for p in range(len(lph)):
+            assert abs(lph[p] - (0.0 if p in last else -np.log(V))) < 1e-3
+            assert abs(enth[p] - np.log(V)) < 1e-3
+    finally:
+        case.close()
+
+
+def test_gather_grpo_full(gpu_lib):
+    w = get_workload("grpo")
+    _run(gpu_lib, w.seqs, w.max_tokens_per_mb, w.vocab, w.dtype, w.seed, std=w.logit_std)
+
+
+def test_gather_bimodal_sampled(gpu_lib):
+    w = get_workload("bimodal")
+    seqs = w.seqs
+    case_trees = oracle.build_forest(seqs, w.max_tokens_per_mb).trees
+    # keep three trees' sequences only: the gather is per tree
+    keep = set(case_trees[0].seq_ids) | set(case_trees[5].seq_ids) | set(case_trees[-1].seq_ids)
+    sub = [s for i, s in enumerate(seqs) if i in keep]
+    _run(gpu_lib, sub, w.max_tokens_per_mb, w.vocab, w.dtype, w.seed, std=w.logit_std, seq_sample=4)
+
+
+def test_gather_rejects_out_of_vocab(gpu_lib):
+    import torch
+    case = Case(worked_example(), 128)
+    try:
+        logits = torch.zeros((128, 8), dtype=torch.float32, device="cuda")  # token 8 needs V > 8
+        with pytest.raises(gpu_lib.PstError) as e:
+            gpu_lib.gather_tree_logprobs_entropy(logits, case.metas[0])
+        assert e.value.name == "PST_EINVAL"
+    finally:
+        case.close()
