@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the prefix-shared tree-training hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic sequences:
+  pack the sequences into tries (host, C++), upload each tree's metadata,
+  tree attention forward (and backward when the workload trains), and the
+  logprob/entropy gather when the workload has logits -- all through the C ABI.
+Q/K/V/dO/logits are resident in HBM before the timed region starts.
+
+Default workload: GRPO group packing (4 prompts x 512 tokens, 8 responses of
+U{128..1024} tokens, 8192-token trees, bf16, 32 query / 8 key-value heads,
+head_dim 128, forward + gather over a 32000-token vocab).
+
+Prints ONE JSON line.  `value` is the tree-attention effective TFLOP/s
+(forward, plus backward when timed): algorithmic FLOPs -- 4*d*Hq per visible
+(query, key) pair forward, 2.5x that backward -- over the attention kernels'
+time measured with HIP events on the launch stream.  ms_per_step is the wall
+clock of a whole step.  The gather's GB/s, packed tokens/s and the tree token
+ratio ride along; `roofline` describes the kernel that takes the most time,
+`cpu_baseline` the oracle timed on a bounded sample on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-attn effective TFLOP/s (fwd/bwd) at 8K-token trees; logprob-gather GB/s"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA peaks of MI355X
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="grpo",
+                    help="tiny | grpo | agentic | bimodal | long | long_control")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import prefix_shared_tree_packed_amd as pst
+    from workloads import get_workload, make_tensor, tree_tensor_seed
+
+    pst.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w = get_workload(args.workload)
+    log(f"workload {w.name}: {len(w.seqs)} sequences, {w.n_tokens} tokens")
+
+    shape_forest = pst.build_tree(w.seqs, w.max_tokens_per_mb)
+    stats = shape_forest.stats()
+    sizes = [shape_forest.sizes(t) for t in range(shape_forest.n_trees)]
+    n_trees = len(sizes)
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    d, hq, hkv = w.head_dim, w.hq, w.hkv
+
+    bufs = []
+    for t, s in enumerate(sizes):
+        Np = s["n_padded"]
+        b = {}
+        b["q"] = make_tensor((Np, hq, d), w.dtype, tree_tensor_seed(w.seed, t, "q"), dev)
+        b["k"] = make_tensor((Np, hkv, d), w.dtype, tree_tensor_seed(w.seed, t, "k"), dev)
+        b["v"] = make_tensor((Np, hkv, d), w.dtype, tree_tensor_seed(w.seed, t, "v"), dev)
+        b["o"] = torch.empty((Np, hq, d), dtype=tdt, device=dev)
+        b["lse"] = torch.empty((hq, Np), dtype=torch.float32, device=dev)
+        if w.bwd:
+            b["do"] = make_tensor((Np, hq, d), w.dtype, tree_tensor_seed(w.seed, t, "do"), dev)
+            b["dq"] = torch.empty_like(b["q"])
+            b["dk"] = torch.empty_like(b["k"])
+            b["dv"] = torch.empty_like(b["v"])
+            b["ws"] = torch.empty((hq, Np), dtype=torch.float32, device=dev)
+        if w.gather:
+            b["logits"] = make_tensor((Np, w.vocab), w.dtype, tree_tensor_seed(w.seed, t, "logits"),
+                                      dev, std=w.logit_std)
+            b["lp"] = torch.empty(s["n_out"], dtype=torch.float32, device=dev)
+            b["ent"] = torch.empty(s["n_out"], dtype=torch.float32, device=dev)
+        bufs.append(b)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(record):
+        forest = pst.build_tree(w.seqs, w.max_tokens_per_mb)
+        metas = [pst.tree_meta_create(forest, t, stream) for t in range(forest.n_trees)]
+        evs = []
+        for t, m in enumerate(metas):
+            b = bufs[t]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+            if record:
+                e[0].record(stream)
+            pst.tree_attn_fwd(b["q"], b["k"], b["v"], m, out=b["o"], lse=b["lse"], stream=stream)
+            if record:
+                e[1].record(stream)
+            if w.bwd:
+                pst.tree_attn_bwd(b["q"], b["k"], b["v"], b["o"], b["lse"], b["do"], m,
+                                  dq=b["dq"], dk=b["dk"], dv=b["dv"], workspace=b["ws"], stream=stream)
+            if record:
+                e[2].record(stream)
+            if w.gather:
+                pst.gather_tree_logprobs_entropy(b["logits"], m, logprobs=b["lp"], entropy=b["ent"],
+                                                 stream=stream)
+            if record:
+                e[3].record(stream)
+            evs.append(e)
+        return forest, metas, evs
+
+    def release(items):
+        torch.cuda.synchronize()
+        for forest, metas, _ in items:
+            for m in metas:
+                m.destroy()
+            forest.close()
+
+    log(f"{n_trees} trees; warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        release([step(False)])
+
+    # host packing alone, for the record
+    t0 = time.perf_counter()
+    for _ in range(5):
+        pst.build_tree(w.seqs, w.max_tokens_per_mb).close()
+    host_build_ms = (time.perf_counter() - t0) / 5 * 1e3
+
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    done = [step(True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+
+    fwd_ms, bwd_ms, gat_ms = [], [], []
+    for _, _, evs in done:
+        for e in evs:
+            fwd_ms.append(e[0].elapsed_time(e[1]))
+            bwd_ms.append(e[1].elapsed_time(e[2]))
+            gat_ms.append(e[2].elapsed_time(e[3]))
+    release(done)
+
+    K = args.steps
+    pairs = stats["n_pairs"]
+    fwd_flops = 4.0 * d * hq * pairs
+    bwd_flops = 2.5 * fwd_flops if w.bwd else 0.0
+    fwd_t = sum(fwd_ms) / K * 1e-3           # seconds of forward kernels per step
+    bwd_t = sum(bwd_ms) / K * 1e-3
+    gat_t = sum(gat_ms) / K * 1e-3
+    attn_tflops = (fwd_flops + bwd_flops) / (fwd_t + bwd_t) / 1e12
+    kernels = {"attn_fwd": {"ms_per_step": fwd_t * 1e3, "TFLOP/s": fwd_flops / fwd_t / 1e12,
+                            "launches_per_step": n_trees}}
+    if w.bwd:
+        kernels["attn_bwd"] = {"ms_per_step": bwd_t * 1e3, "TFLOP/s": bwd_flops / bwd_t / 1e12,
+                               "launches_per_step": n_trees}
+    gather_bytes = 0
+    if w.gather:
+        esz = 4 if w.dtype == "f32" else 2
+        n_out = sum(s["n_out"] for s in sizes)
+        n_real = stats["tree_tokens"]
+        # logits of every real row once + two fp32 outputs and the row->output map
+        gather_bytes = n_real * w.vocab * esz + n_out * (4 + 4 + 4 + 4) + 4 * (n_real + n_trees)
+        kernels["gather"] = {"ms_per_step": gat_t * 1e3, "GB/s": gather_bytes / gat_t / 1e9,
+                             "launches_per_step": n_trees}
+
+    # roofline of the kernel that takes the most time
+    cands = [("attn_fwd", fwd_t), ("attn_bwd", bwd_t), ("gather", gat_t)]
+    dom = max((c for c in cands if c[0] in kernels), key=lambda c: c[1])[0]
+    if dom == "gather":
+        ach = gather_bytes / gat_t / 1e9
+        roof = {"kernel": "gather", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS, "traffic": None,
+                "algorithmic_per_launch": gather_bytes / n_trees}
+    else:
+        fl, tt = (fwd_flops, fwd_t) if dom == "attn_fwd" else (bwd_flops, bwd_t)
+        ach = fl / tt / 1e12
+        peak = PEAK_TFLOPS[w.dtype]
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                "frac": ach / peak, "traffic": None, "algorithmic_per_launch": fl / n_trees}
+
+    out = {
+        "metric": METRIC,
+        "value": attn_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "sequences": len(w.seqs), "orig_tokens": stats["orig_tokens"],
+            "max_tokens_per_mb": w.max_tokens_per_mb, "trees": n_trees,
+            "hq": hq, "hkv": hkv, "head_dim": d, "vocab": w.vocab,
+            "passes": "+".join(p for p, on in (("fwd", w.fwd), ("bwd", w.bwd), ("gather", w.gather)) if on),
+        },
+        "tree_token_ratio": stats["tree_token_ratio"],
+        "packed_tokens_per_s": stats["tree_tokens"] / (ms_per_step * 1e-3),
+        "gather_GBps": kernels["gather"]["GB/s"] if w.gather else None,
+        "visible_pairs": pairs,
+        "causal_pairs": stats["causal_pairs"],
+        "tiles": stats["n_tiles"],
+        "tile_utilisation": pairs / (stats["n_tiles"] * 128 * 128),
+        "host_build_ms": host_build_ms,
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        bcopy = torch.empty_like(a)
+        torch.cuda.synchronize()
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = n * 4
+        del a, bcopy
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, sizes, bufs, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, sizes, bufs, target_s):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    the dense-mask float64 forward of tree 0 for as many query heads of the
+    first key/value group as fit in about `target_s` seconds (at least one),
+    reported in the same algorithmic-FLOP unit as `value`."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    ref = oracle.build_forest(w.seqs, w.max_tokens_per_mb)
+    tree = ref.trees[0]
+    G = w.hq // w.hkv
+    b = bufs[0]
+    h64 = lambda x: x.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    mask = oracle.dense_mask(tree)
+    # whole key/value groups of query heads (group g serves heads g*G .. g*G+G-1)
+    # until the projected time passes target_s
+    elapsed, groups = 0.0, 0
+    while groups < w.hkv and (groups == 0 or elapsed * (groups + 1) / groups < target_s):
+        qq = h64(b["q"][:, groups * G:(groups + 1) * G])
+        kk = h64(b["k"][:, groups:groups + 1])
+        vv = h64(b["v"][:, groups:groups + 1])
+        s0 = time.perf_counter()
+        oracle.attn_fwd(tree, qq, kk, vv, mask=mask)
+        elapsed += time.perf_counter() - s0
+        groups += 1
+    heads = groups * G
+    flops = 4.0 * w.head_dim * heads * tree.n_pairs
+    res = {
+        "value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"dense-mask float64 forward of tree 0 ({tree.n_tokens} tokens), "
+                  f"{heads} of {w.hq} query heads, {elapsed:.1f} s",
+        "host_cpus": os.cpu_count(),
+    }
+    if w.gather:
+        sids = tree.seq_ids[:2]
+        rows = np.concatenate([tree.seq_index[s] for s in sids])
+        uniq = np.unique(rows)
+        x = h64(b["logits"][torch.as_tensor(uniq, device=b["logits"].device)])
+        sub = oracle.Tree(**{**tree.__dict__, "seq_ids": sids,
+                             "seq_index": {s: np.searchsorted(uniq, tree.seq_index[s]) for s in sids}})
+        s0 = time.perf_counter()
+        oracle.gather_logprobs_entropy(sub, w.seqs, x)
+        gs = time.perf_counter() - s0
+        res["gather_GBps"] = len(rows) * w.vocab * (4 if w.dtype == "f32" else 2) / gs / 1e9
+        res["gather_sample"] = f"{len(sids)} sequences ({len(rows)} rows of {w.vocab} logits), {gs:.2f} s"
+    return res
+
+
+if __name__ == "__main__":
+    main()

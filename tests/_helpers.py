@@ -2,9 +2,20 @@
 and the oracle, draw seeded inputs on the device, compare with tolerances.
 
 Tolerances (float outputs; integer outputs are compared bit-exactly):
-  fp32 attention:  |got - ref| <= 1e-5 |ref| + 1e-6
-  bf16 attention:  |got - ref| <= 2e-2 (O, LSE, dQ, dK, dV)
-  logprob/entropy: |got - ref| <= 1e-3 from bf16 logits, 1e-5 |ref| + 1e-6 from fp32
+  fp32 attention O, LSE:  |got - ref| <= 1e-5 |ref| + 1e-6
+  bf16 attention O, LSE:  |got - ref| <= 2e-2
+  fp32 gradients:         |got - ref| <= 1e-5 (|ref| + max|ref|)
+  bf16 gradients:         |got - ref| <= 2e-2 + 2^-8 |ref|
+  logprob/entropy:        |got - ref| <= 1e-3 from bf16 logits, 1e-5 |ref| + 1e-6 from fp32
+
+The gradient bounds follow from the arithmetic.  dS = P (dP - D) subtracts
+two fp32 dot products of the same size, so a gradient that is exactly zero
+(a pad row or a token that sees only itself) comes out at fp32 rounding of
+the tensor's scale, not of the element: the fp32 bound is the element-wise
+relative one plus the norm-wise one (relative to the tensor's largest value).  A bf16 gradient is rounded once on output
+(half an ulp, at most 2^-8 of its magnitude) on top of the bf16 rounding of
+P in its products; heavily shared prefix tokens reach |dV| of several units,
+where the output rounding alone exceeds 2e-2.
 """
 
 from __future__ import annotations
@@ -20,14 +31,19 @@ def tol(dtype):
     return (1e-5, 1e-6) if dtype == "f32" else (0.0, 2e-2)
 
 
-def assert_close(got, ref, dtype, what, rtol=None, atol=None):
+def assert_close(got, ref, dtype, what, rtol=None, atol=None, grad=False):
     r, a = tol(dtype)
     r = r if rtol is None else rtol
     a = a if atol is None else atol
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     err = np.abs(got - ref)
-    bound = a + r * np.abs(ref)
+    if grad and dtype == "f32":
+        bound = 1e-5 * (np.abs(ref) + np.abs(ref).max())
+    elif grad:
+        bound = 2e-2 + 2.0 ** -8 * np.abs(ref)
+    else:
+        bound = a + r * np.abs(ref)
     bad = err > bound
     if bad.any():
         idx = np.unravel_index(np.argmax(err - bound), err.shape)

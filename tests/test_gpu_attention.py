@@ -120,9 +120,9 @@ def _bwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, seed):
             o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[t])
             dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[t])
             rdq, rdk, rdv = oracle.attn_bwd(tree, host(q), host(k), host(v), host(do))
-            assert_close(host(dq), rdq, dtype, "dQ")
-            assert_close(host(dk), rdk, dtype, "dK")
-            assert_close(host(dv), rdv, dtype, "dV")
+            assert_close(host(dq), rdq, dtype, "dQ", grad=True)
+            assert_close(host(dk), rdk, dtype, "dK", grad=True)
+            assert_close(host(dv), rdv, dtype, "dV", grad=True)
     finally:
         case.close()
 
@@ -186,11 +186,11 @@ def test_bwd_agentic_sampled(gpu_lib):
                 heads = list(range(g * G, (g + 1) * G))
                 rq, rkv = oracle.attn_bwd_rows(tree, qh, kh, vh, doh, rows, keys, (g, heads))
                 assert_close(np.array([dqh[i, h] for (i, h) in rq]), np.array(list(rq.values())),
-                             w.dtype, "dQ[agentic]")
+                             w.dtype, "dQ[agentic]", grad=True)
                 assert_close(np.array([dkh[j, gg] for (j, gg) in rkv]),
-                             np.array([x[0] for x in rkv.values()]), w.dtype, "dK[agentic]")
+                             np.array([x[0] for x in rkv.values()]), w.dtype, "dK[agentic]", grad=True)
                 assert_close(np.array([dvh[j, gg] for (j, gg) in rkv]),
-                             np.array([x[1] for x in rkv.values()]), w.dtype, "dV[agentic]")
+                             np.array([x[1] for x in rkv.values()]), w.dtype, "dV[agentic]", grad=True)
     finally:
         case.close()
 
