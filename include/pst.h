@@ -100,6 +100,9 @@ typedef struct {
   int32_t* q_ptr;           /* [n_blocks+1] CSR of non-empty tiles per query block */
   int32_t* q_kb;            /* [n_tiles] key block of each tile, descending per query block */
   int32_t* q_full;          /* [n_tiles] 1 if every pair of the tile is visible */
+  int32_t* q_cls;           /* [n_tiles] class of each 32x32 sub-block of the tile,
+                               2 bits at bit 2*(4*qs+ks) for query sub-block qs and
+                               key sub-block ks: 0 no visible pair, 1 some, 2 all */
   int32_t* kb_qhi;          /* [n_blocks] last query block that sees each key block
                                (the visible query blocks are kb..kb_qhi[kb]) */
   int32_t* fwd_order;       /* [n_blocks] query blocks by descending tile count */

@@ -99,6 +99,9 @@ class Tree:
     q_ptr: np.ndarray          # [nb+1] int32, non-empty tiles of each query block
     q_kb: np.ndarray           # [n_tiles] int32 key block, descending within a query block
     q_full: np.ndarray         # [n_tiles] int32 1 if every pair of the tile is visible
+    q_cls: np.ndarray          # [n_tiles] int32: 2 bits per 32x32 sub-block (query
+                               #   sub-block qs, key sub-block ks) at bit 2*(4*qs+ks):
+                               #   0 no visible pair, 1 some, 2 all
     kb_qhi: np.ndarray         # [nb] int32 last query block that sees the key block
     fwd_order: np.ndarray      # [nb] query blocks by tile count desc, then index
     bwd_order: np.ndarray      # [nb] key blocks by tile count desc, then index
@@ -287,28 +290,50 @@ def _walk_ancestors(N: int, Np: int, parent: np.ndarray):
     each 128x128 block of the mask is classified by how many of its pairs are
     visible (none: empty, all: full, else partial)."""
     nb = Np // BLOCK
-    subtree_end = np.arange(Np, dtype=np.int64)
-    count = np.zeros(nb * nb, dtype=np.int64)
-    q = np.arange(N, dtype=np.int64)
+    n32 = Np // 32
+    subtree_end = np.arange(Np, dtype=np.int32)
+    count32 = np.zeros(n32 * n32, dtype=np.int64)   # visible pairs per 32x32 block
+    q = np.arange(N, dtype=np.int32)
     cur = q.copy()
     n_pairs = 0
+    pending, n_pending = [], 0
+
+    def flush():
+        nonlocal count32, pending, n_pending
+        if pending:
+            ids = np.concatenate(pending)
+            count32 += np.bincount(ids, minlength=n32 * n32)
+        pending, n_pending = [], 0
+
     while q.size:
         np.maximum.at(subtree_end, cur, q)
-        count += np.bincount((q // BLOCK) * nb + cur // BLOCK, minlength=nb * nb)
+        pending.append((q >> 5).astype(np.int64) * n32 + (cur >> 5))
+        n_pending += q.size
+        if n_pending > (1 << 25):
+            flush()
         n_pairs += q.size
-        nxt = parent[cur].astype(np.int64)
+        nxt = parent[cur]
         keep = nxt >= 0
         q, cur = q[keep], nxt[keep]
+    flush()
     pads = np.arange(N, Np, dtype=np.int64)
-    count += np.bincount((pads // BLOCK) * nb + pads // BLOCK, minlength=nb * nb)
-    count = count.reshape(nb, nb)     # [query block, key block]
+    count32 += np.bincount((pads >> 5) * n32 + (pads >> 5), minlength=n32 * n32)
+    count32 = count32.reshape(n32, n32)              # [query sub-block, key sub-block]
+    count = count32.reshape(nb, 4, nb, 4).sum(axis=(1, 3))   # [query block, key block]
 
-    q_ptr, q_kb, q_full = [0], [], []
+    q_ptr, q_kb, q_full, q_cls = [0], [], [], []
     for qb in range(nb):
         for kb in range(nb - 1, -1, -1):
             if count[qb, kb] > 0:
                 q_kb.append(kb)
                 q_full.append(1 if count[qb, kb] == BLOCK * BLOCK else 0)
+                bits = 0
+                for qs in range(4):
+                    for ks in range(4):
+                        n = count32[4 * qb + qs, 4 * kb + ks]
+                        cls = 0 if n == 0 else (2 if n == 32 * 32 else 1)
+                        bits |= cls << (2 * (4 * qs + ks))
+                q_cls.append(bits)
         q_ptr.append(len(q_kb))
     kb_qhi = np.array([max(qb for qb in range(nb) if count[qb, kb] > 0)
                        for kb in range(nb)], dtype=np.int32)
@@ -319,6 +344,7 @@ def _walk_ancestors(N: int, Np: int, parent: np.ndarray):
     return subtree_end.astype(np.int32), dict(
         q_ptr=np.array(q_ptr, np.int32), q_kb=np.array(q_kb, np.int32),
         q_full=np.array(q_full, np.int32), kb_qhi=kb_qhi,
+        q_cls=np.array(q_cls, np.uint32).view(np.int32),
         fwd_order=np.array(fwd_order, np.int32),
         bwd_order=np.array(bwd_order, np.int32), n_pairs=int(n_pairs),
     )

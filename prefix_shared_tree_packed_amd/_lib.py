@@ -35,7 +35,7 @@ P64 = POINTER(c_int64)
 ARRAY_FIELDS = [
     "token", "pos", "parent", "subtree_end", "node", "node_start", "node_end",
     "node_parent", "node_seq_ptr", "node_seq_ids", "seq_ids", "seq_out_offsets",
-    "seq_index", "child_ptr", "child_idx", "q_ptr", "q_kb", "q_full", "kb_qhi",
+    "seq_index", "child_ptr", "child_idx", "q_ptr", "q_kb", "q_full", "q_cls", "kb_qhi",
     "fwd_order", "bwd_order",
 ]
 

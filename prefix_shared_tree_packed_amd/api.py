@@ -102,6 +102,7 @@ class Forest:
             "seq_ids": s["n_seqs"], "seq_out_offsets": s["n_seqs"] + 1,
             "seq_index": s["n_out"], "child_ptr": s["n_tokens"] + 1, "child_idx": s["n_edges"],
             "q_ptr": s["n_blocks"] + 1, "q_kb": s["n_tiles"], "q_full": s["n_tiles"],
+            "q_cls": s["n_tiles"],
             "kb_qhi": s["n_blocks"], "fwd_order": s["n_blocks"], "bwd_order": s["n_blocks"],
         }
         out, a = {}, _lib.TreeArrays()

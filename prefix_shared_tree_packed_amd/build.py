@@ -35,6 +35,7 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 HIP_SOURCES = [
     "capi.cpp",
     "kernels/attn_fwd.hip",
+    "kernels/attn_fwd_bf16.hip",
     "kernels/attn_bwd.hip",
     "kernels/gather.hip",
 ]

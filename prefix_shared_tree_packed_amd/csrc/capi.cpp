@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -18,8 +19,10 @@ struct pst_forest {
 
 // Device layout of one tree's metadata: a single int32 allocation holding
 // se [Np] | q_ptr [nb+1] | q_tile [n_tiles] | kb_qhi [nb] | fwd_order [nb] |
-// bwd_order [nb] | row_out_ptr [N+1] | out_pos [n_out] | out_tgt [n_out],
-// every section starting on a 16-byte boundary.  The pinned staging copy is
+// bwd_order [nb] | row_out_ptr [N+1] | out_pos [n_out] | out_tgt [n_out] |
+// blk32 [Np/32][2] (min, max subtree end of each 32-key block) |
+// q_cls [n_tiles] (32x32 sub-block classes of each tile), every
+// section starting on a 16-byte boundary.  The pinned staging copy is
 // kept until destroy so the asynchronous upload never reads freed memory.
 struct pst_tree_meta {
   int device = -1;
@@ -186,6 +189,7 @@ int pst_forest_export_tree(const pst_forest* forest, int32_t tree, const pst_tre
   copy_out(a->q_ptr, t.q_ptr);
   copy_out(a->q_kb, t.q_kb);
   copy_out(a->q_full, t.q_full);
+  copy_out(a->q_cls, t.q_cls);
   copy_out(a->kb_qhi, t.kb_qhi);
   copy_out(a->fwd_order, t.fwd_order);
   copy_out(a->bwd_order, t.bwd_order);
@@ -239,6 +243,8 @@ int pst_tree_meta_create(const pst_forest* forest, int32_t tree, void* stream,
   const size_t o_rptr = off;      off += round4(static_cast<size_t>(t.N) + 1);
   const size_t o_opos = off;      off += round4(n_out);
   const size_t o_otgt = off;      off += round4(n_out);
+  const size_t o_blk = off;       off += round4(static_cast<size_t>(t.Np) / 16);
+  const size_t o_qcls = off;      off += round4(n_tiles);
   const size_t words = off;
 
   pst_tree_meta* m = new (std::nothrow) pst_tree_meta;
@@ -272,6 +278,16 @@ int pst_tree_meta_create(const pst_forest* forest, int32_t tree, void* stream,
     std::memcpy(h + o_opos, t.out_pos.data(), n_out * 4);
     std::memcpy(h + o_otgt, t.out_tgt.data(), n_out * 4);
   }
+  if (n_tiles) std::memcpy(h + o_qcls, t.q_cls.data(), n_tiles * 4);
+  for (int32_t b = 0; b < t.Np / 32; ++b) {
+    int32_t lo = t.se[32 * b], hi = t.se[32 * b];
+    for (int32_t j = 32 * b + 1; j < 32 * b + 32; ++j) {
+      lo = std::min(lo, t.se[j]);
+      hi = std::max(hi, t.se[j]);
+    }
+    h[o_blk + 2 * b] = lo;
+    h[o_blk + 2 * b + 1] = hi;
+  }
   e = hipMemcpyAsync(m->dbuf, h, words * sizeof(int32_t), hipMemcpyHostToDevice,
                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -284,8 +300,8 @@ int pst_tree_meta_create(const pst_forest* forest, int32_t tree, void* stream,
   fill_sizes(t, &m->sizes);
   int32_t* d = m->dbuf;
   m->dev = pst::TreeDev{d + o_se,   d + o_qptr, d + o_qtile, d + o_qhi,  d + o_ford,
-                        d + o_bord, d + o_rptr, d + o_opos,  d + o_otgt, t.N,
-                        t.Np,       t.nb,       static_cast<int32_t>(n_tiles)};
+                        d + o_bord, d + o_rptr, d + o_opos,  d + o_otgt, d + o_blk, d + o_qcls,
+                        t.N,        t.Np,       t.nb,        static_cast<int32_t>(n_tiles)};
   m->min_target = t.min_target;
   m->max_target = t.max_target;
   *out = m;

@@ -219,6 +219,25 @@ void flatten(const Trie& trie, int32_t tid, const int32_t* tokens, const int64_t
   t.q_ptr.assign(1, 0);
   t.q_kb.clear();
   t.q_full.clear();
+  t.q_cls.clear();
+  // 32-key blocks: min and max subtree end.  Query and key sub-blocks share
+  // the 32-alignment, so a key sub-block is entirely before, equal to, or
+  // entirely after a query sub-block, and its class follows from the range
+  // rule exactly as for whole tiles.
+  const int32_t nb32 = Np / 32;
+  std::vector<int32_t> smin32(nb32), smax32(nb32);
+  for (int32_t b = 0; b < nb32; ++b) {
+    const auto s0 = t.se.begin() + 32 * b;
+    smin32[b] = *std::min_element(s0, s0 + 32);
+    smax32[b] = *std::max_element(s0, s0 + 32);
+  }
+  auto sub_class = [&](int32_t qlo, int32_t kbase) {
+    const int32_t qhi = qlo + 31;
+    const int32_t b = kbase / 32;
+    if (kbase > qhi || smax32[b] < qlo) return 0;
+    if (kbase + 31 <= qlo && smin32[b] >= qhi) return 2;
+    return 1;
+  };
   std::vector<int32_t> per_q(nb, 0), per_k(nb, 0);
   for (int32_t qb = 0; qb < nb; ++qb) {
     const int32_t first = qb * kBlock, last = first + kBlock - 1;
@@ -226,6 +245,11 @@ void flatten(const Trie& trie, int32_t tid, const int32_t* tokens, const int64_t
       if (kb < qb && kmax[kb] < first) continue;
       t.q_kb.push_back(kb);
       t.q_full.push_back(kb < qb && kmin[kb] >= last ? 1 : 0);
+      uint32_t bits = 0;
+      for (int32_t qs = 0; qs < 4; ++qs)
+        for (int32_t ks = 0; ks < 4; ++ks)
+          bits |= static_cast<uint32_t>(sub_class(first + 32 * qs, kb * kBlock + 32 * ks)) << (2 * (4 * qs + ks));
+      t.q_cls.push_back(static_cast<int32_t>(bits));
       per_q[qb]++;
       per_k[kb]++;
     }

@@ -35,6 +35,9 @@ struct Tree {
   std::vector<int32_t> child_ptr, child_idx;
   // 128x128 tile structure
   std::vector<int32_t> q_ptr, q_kb, q_full, kb_qhi, fwd_order, bwd_order;
+  // per tile: class of each 32x32 sub-block (query sub-block qs, key sub-block
+  // ks) in bits 2*(4*qs+ks) .. +1: 0 no visible pair, 1 some, 2 all
+  std::vector<int32_t> q_cls;
   // gather map: for each real row, the outputs that read it
   std::vector<int32_t> row_out_ptr;  // [N+1]
   std::vector<int32_t> out_pos;      // [n_out] output slot

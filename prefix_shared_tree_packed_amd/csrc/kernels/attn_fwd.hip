@@ -19,6 +19,9 @@
 // for the slot->key map).  Online softmax in the exp2 domain, fp32
 // accumulation; with bf16 inputs P is rounded to bf16 before the P.V product.
 //
+// This file holds the generic instance (fp32, and bf16 with head_dim 64);
+// bf16 with head_dim 128 runs the specialised kernel of attn_fwd_bf16.hip.
+//
 // Workgroups are ordered heaviest query block first (longest-processing-time
 // order from the encoder) and grouped by key/value head per XCD, so the
 // query heads sharing a K/V head run on one XCD and share its L2.
@@ -210,7 +213,7 @@ hipError_t launch_attn_fwd(int dtype, int head_dim, const void* q, const void* k
                            void* o, float* lse, const TreeDev& tr, int hq, int hkv, float scale,
                            hipStream_t stream) {
   if (dtype == kDtypeBf16) {
-    if (head_dim == 128) return launch<bf16_t, 128>(q, k, v, o, lse, tr, hq, hkv, scale, stream);
+    if (head_dim == 128) return launch_attn_fwd_bf16_d128(q, k, v, o, lse, tr, hq, hkv, scale, stream);
     if (head_dim == 64) return launch<bf16_t, 64>(q, k, v, o, lse, tr, hq, hkv, scale, stream);
   } else {
     // fp32 is built for head_dim 64 only, like the backward pass

@@ -1,0 +1,300 @@
+// Tree attention forward pass, bf16 with head_dim 128: the performance path
+// on gfx950.  Same mathematics and work decomposition as attn_fwd.hip (one
+// workgroup per 128-row query block and query head, four waves of 32 rows,
+// S^T = K.Q^T with the query in the lane, O^T += V^T.P^T fed from the score
+// accumulators); what changes is how every step is fed:
+//
+//  * Each non-empty 128x128 tile is walked as two 64-key halves through a
+//    double-buffered LDS pipeline: while the waves compute one half, the next
+//    half's K rows stream global -> LDS directly (global_load_lds_dwordx4: no
+//    VGPRs, no VALU) and its V rows are already in registers.  One barrier per
+//    half; two 32 KB buffers keep two workgroups per CU.
+//  * K rows are 256 bytes with the 16-byte chunk c of row r stored at c ^ (r & 15).
+//  * V is transposed in registers (4 keys x 8 dims per thread, v_perm_b32)
+//    into d-major rows whose keys are permuted inside each group of 16 (key
+//    16t+8a+4h+j sits at 16t+8h+4a+j), so every MFMA operand of V^T is ONE
+//    16-byte LDS read; the 16-byte chunk c of row d sits at c ^ ((d >> 1) & 7),
+//    which keeps those reads bank-conflict free.
+//  * The mask is evaluated per (wave, 32-key block): a block whose keys no
+//    query of the wave sees is skipped (no MFMA, no exp), a block every query
+//    sees runs unmasked, and only the rest pay the per-element test
+//    (unsigned)(i - j) <= se[j] - j, three VALU ops.
+//  * Scores stay unscaled; the softmax scale is folded into the exponent's
+//    FMA, and the running max is refreshed lazily: O and the row sum are
+//    rescaled only when a row's max grows by more than 2^8, so exponentials
+//    stay below 256 and most steps skip the rescale.
+#include "launch.h"
+#include "mfma.h"
+
+#include <cmath>
+
+namespace pst {
+namespace {
+
+constexpr int D = 128;
+constexpr int kHalf = 64;                 // keys per pipeline step
+constexpr int kKRow = D * 2;              // K row: 256 B
+constexpr int kVRow = kHalf * 2;          // V^T row: 128 B (64 keys)
+constexpr int kBufBytes = kHalf * kKRow;  // 16 KB for K, 16 KB for V^T
+constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only: scalar loads
+
+__device__ __forceinline__ cint32* cst(const int32_t* p) { return (cint32*)(p); }
+
+__device__ __forceinline__ uint32_t word(const uint4& u, int p) {
+  return p == 0 ? u.x : p == 1 ? u.y : p == 2 ? u.z : u.w;
+}
+
+__device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int byte_off) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + byte_off));
+}
+
+__global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    bf16_t* __restrict__ o, float* __restrict__ lse, TreeDev tr, int hq, int hkv, float c) {
+  using M = Mfma<bf16_t>;
+  // two separately named buffers (not one array indexed by the step parity)
+  // so the compiler can tell the in-flight DMA target from the buffer being
+  // read and does not drain the prefetch before every LDS read
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt_lds0[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt_lds1[kBufBytes];
+  __shared__ __attribute__((aligned(16))) int32_t span_lds0[kHalf];
+  __shared__ __attribute__((aligned(16))) int32_t span_lds1[kHalf];
+
+  const int G = hq / hkv;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_g = G * tr.nb;
+  const int g = logical / per_g;
+  const int rem = logical - g * per_g;
+  const int rank = rem / G;
+  const int h = g * G + (rem - rank * G);
+  const int qb = cst(tr.fwd_order)[rank];
+
+  const int tid = threadIdx.x;
+  // wave index as a scalar, so the per-wave block classes branch on SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int lq = lane % 32;
+  const int half = lane / 32;
+  const int qlo = qb * kTile + wave * 32;  // first query row of this wave
+  const int qrow = qlo + lq;
+
+  bf16x8_t qf[8];
+  {
+    const bf16_t* qp = q + (static_cast<size_t>(qrow) * hq + h) * D + half * 8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = M::load(qp + 16 * s);
+  }
+  // LDS byte offsets of this lane's 16-byte operand chunks: K rows for
+  // contraction step s, V^T rows for 16-key step s
+  int koff_rd[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) koff_rd[s] = lq * kKRow + (((2 * s + half) ^ (lq & 15)) << 4);
+  int voff_rd[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) voff_rd[s] = lq * kVRow + (((2 * s + half) ^ ((lq >> 1) & 7)) << 4);
+
+  // Global loads: a wave-uniform base pointer plus a 32-bit lane offset.
+  const uint32_t kv_bytes = static_cast<uint32_t>(hkv) * D * 2;  // one token's K (or V) rows
+  const char* kgb = reinterpret_cast<const char*>(k + static_cast<size_t>(g) * D);
+  const char* vgb = reinterpret_cast<const char*>(v + static_cast<size_t>(g) * D);
+  // K: wave instruction i writes rows 4(4*wave+i) .. +3 of the half, lane ->
+  // row +lane/16, stored chunk lane%16 holding logical chunk (lane%16)^(row&15)
+  uint32_t koff_ld[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    koff_ld[i] = (lane >> 4) * kv_bytes + (((lane & 15) ^ ((4 * i + (lane >> 4)) & 15)) << 4);
+  // V: this thread stages keys 4*kq .. 4*kq+3 of the half, dims 8*vcc .. +7
+  const int kq = lane & 15;
+  const int vcc = tid >> 4;
+  const uint32_t voff_ld = 4 * kq * kv_bytes + vcc * 16;
+  // stored key position of the quad: key 16t+8a+4h (+j) -> 16t+8h+4a (+j)
+  const int vpos = 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) oacc[b] = f32x16_t{};
+  float m_used = -INFINITY, l = 0.f;
+
+  cint32* q_ptr = cst(tr.q_ptr);
+  cint32* q_tile = cst(tr.q_tile);
+  cint32* q_cls = cst(tr.q_cls);
+  const int t_begin = q_ptr[qb];
+  const int n_steps = 2 * (q_ptr[qb + 1] - t_begin);
+  // tile index of a step, pinned to an SGPR so metadata reads stay scalar
+  auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + (st >> 1)); };
+  auto step_key0 = [&](int st) { return (q_tile[tile_of(st)] >> 1) * kTile + kHalf * (st & 1); };
+
+  uint4 vreg[4];
+  int4 se4 = make_int4(0, 0, 0, 0);
+  auto issue_loads = [&](int st, uint8_t* kdst) {
+    const int k0 = step_key0(st);
+    const char* kt = kgb + static_cast<size_t>(k0) * kv_bytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(kt + static_cast<size_t>(4 * (4 * wave + i)) * kv_bytes + koff_ld[i],
+                                       (lds_void*)(kdst + (4 * wave + i) * 1024), 16, 0, 0);
+    const char* vt = vgb + static_cast<size_t>(k0) * kv_bytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      vreg[j] = *reinterpret_cast<const uint4*>(vt + static_cast<size_t>(j) * kv_bytes + voff_ld);
+    // every lane loads (lanes past 16 repeat a quad; only 16 are stored), so
+    // no load sits in a divergent branch
+    se4 = *reinterpret_cast<const int4*>(tr.se + k0 + 4 * (tid & 15));
+  };
+  auto store_v = [&](int st, uint8_t* vdst, int32_t* sdst) {
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+      const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+      uint2 outv;
+      outv.x = __builtin_amdgcn_perm(word(vreg[1], mm >> 1), word(vreg[0], mm >> 1), sel);
+      outv.y = __builtin_amdgcn_perm(word(vreg[3], mm >> 1), word(vreg[2], mm >> 1), sel);
+      const int d = 8 * vcc + mm;
+      const int chunk = (vpos >> 3) ^ ((d >> 1) & 7);
+      *reinterpret_cast<uint2*>(vdst + d * kVRow + (chunk << 4) + (vpos & 7) * 2) = outv;
+    }
+    if (tid < kHalf / 4) {
+      const int key = step_key0(st) + 4 * tid;
+      const int4 span = make_int4(se4.x - key, se4.y - key - 1, se4.z - key - 2, se4.w - key - 3);
+      *reinterpret_cast<int4*>(sdst + 4 * tid) = span;
+    }
+  };
+
+  auto step = [&](int st, const uint8_t* kcur, const uint8_t* vcur, const int32_t* scur,
+                  uint8_t* knext, uint8_t* vnext, int32_t* snext) {
+    const int k0 = step_key0(st);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // step st staged by every wave; step st-1 consumed
+    // prefetch the next step; after the last step this reloads the last step
+    // into the idle buffer (in bounds, never read) so the code stays
+    // branch-free and the compiler keeps the DMA and the reads apart
+    const int st_next = st + 1 < n_steps ? st + 1 : st;
+    issue_loads(st_next, knext);
+
+    // class of this wave's two 32x32 sub-blocks: 0 empty, 1 partial, 2 full
+    const uint32_t bits = static_cast<uint32_t>(q_cls[tile_of(st)]);
+    int cls[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) cls[kb] = (bits >> (2 * (4 * wave + 2 * (st & 1) + kb))) & 3;
+
+    if (cls[0] | cls[1]) {
+      // S^T = K.Q^T for the non-empty 32-key blocks
+      f32x16_t sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16_t{};
+        if (cls[kb]) {
+#pragma unroll
+          for (int s = 0; s < 8; ++s)
+            sacc[kb] = M::mma(lds_frag(kcur, kb * 32 * kKRow + koff_rd[s]), qf[s], sacc[kb]);
+        }
+      }
+
+      // mask partial blocks; row max of the raw scores
+      float mx = -INFINITY;
+      const int A = qrow - k0 - 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (cls[kb] == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int4 sp = *reinterpret_cast<const int4*>(scur + 32 * kb + 8 * i + 4 * half);
+            const int spv[4] = {sp.x, sp.y, sp.z, sp.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t dlt = static_cast<uint32_t>(A - (32 * kb + 8 * i + j));
+              const float x = dlt <= static_cast<uint32_t>(spv[j]) ? sacc[kb][4 * i + j] : -INFINITY;
+              sacc[kb][4 * i + j] = x;
+              mx = fmaxf(mx, x);
+            }
+          }
+        } else if (cls[kb] == 2) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        }
+      }
+      mx = fmaxf(mx, swap_halves(mx));
+      const float mxc = mx * c;
+      if (__any(mxc > m_used + kRescale)) {
+        const float m_new = fmaxf(m_used, mxc);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_used - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) oacc[b] *= alpha;
+        m_used = m_new;
+      }
+      const float negm = m_used == -INFINITY ? 0.f : -m_used;
+      float sum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (cls[kb]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(sacc[kb][r], c, negm));
+            sacc[kb][r] = p;
+            sum += p;
+          }
+        }
+      }
+      sum += swap_halves(sum);
+      l += sum;
+
+      // O^T += V^T.P^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (cls[kb]) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8_t pf = M::from_acc(sacc[kb], s2);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              oacc[b] = M::mma(lds_frag(vcur, b * 32 * kVRow + voff_rd[2 * kb + s2]), pf, oacc[b]);
+          }
+        }
+      }
+    }
+
+    store_v(st_next, vnext, snext);
+  };
+
+  if (n_steps > 0) {
+    issue_loads(0, k_lds0);
+    store_v(0, vt_lds0, span_lds0);
+  }
+  for (int st = 0; st < n_steps; st += 2) {  // n_steps is even: two halves per tile
+    step(st, k_lds0, vt_lds0, span_lds0, k_lds1, vt_lds1, span_lds1);
+    step(st + 1, k_lds1, vt_lds1, span_lds1, k_lds0, vt_lds0, span_lds0);
+  }
+
+  const float inv = 1.f / l;
+  bf16_t* op = o + (static_cast<size_t>(qrow) * hq + h) * D;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = b * 32 + 8 * i + 4 * half;
+      store4<bf16_t>(op + d, oacc[b][4 * i] * inv, oacc[b][4 * i + 1] * inv,
+                     oacc[b][4 * i + 2] * inv, oacc[b][4 * i + 3] * inv);
+    }
+  if (half == 0)
+    lse[static_cast<size_t>(h) * tr.Np + qrow] = (m_used + fast_log2(l)) * 0.69314718055994531f;
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16_d128(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, const TreeDev& tr, int hq, int hkv, float scale,
+                                     hipStream_t stream) {
+  const float c = scale * 1.4426950408889634f;  // scores in the exp2 domain
+  const dim3 grid(static_cast<unsigned>(tr.nb) * hq);
+  hipLaunchKernelGGL(tree_attn_fwd_bf16_d128, grid, dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                     static_cast<const bf16_t*>(v), static_cast<bf16_t*>(o), lse, tr, hq, hkv, c);
+  return hipGetLastError();
+}
+
+}  // namespace pst

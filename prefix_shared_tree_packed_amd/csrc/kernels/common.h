@@ -32,6 +32,10 @@ struct TreeDev {
   const int32_t* row_out_ptr;  // [N+1] outputs of each real row
   const int32_t* out_pos;      // [n_out] output slot
   const int32_t* out_tgt;      // [n_out] next-token id, -1 for a last token
+  const int32_t* blk32;        // [Np/32][2] min and max subtree end of each 32-key block
+  const int32_t* q_cls;        // [n_tiles] 2-bit class of each 32x32 sub-block (query
+                               // sub-block qs, key sub-block ks at bit 2*(4*qs+ks)):
+                               // 0 no visible pair, 1 some, 2 all
   int32_t N;
   int32_t Np;
   int32_t nb;

@@ -19,6 +19,12 @@ hipError_t launch_attn_fwd(int dtype, int head_dim, const void* q, const void* k
                            void* o, float* lse, const TreeDev& tr, int hq, int hkv, float scale,
                            hipStream_t stream);
 
+// bf16 / head_dim 128 performance kernel (attn_fwd_bf16.hip), reached through
+// launch_attn_fwd.
+hipError_t launch_attn_fwd_bf16_d128(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, const TreeDev& tr, int hq, int hkv, float scale,
+                                     hipStream_t stream);
+
 // workspace: float32 [hq, Np] (the per-row dO.O sums).
 hipError_t launch_attn_bwd(int dtype, int head_dim, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, void* dq, void* dk,

@@ -27,7 +27,7 @@ def compare_forest(seqs, cap):
         assert s["n_tokens"] == rt.n_tokens and s["n_padded"] == rt.n_padded
         assert s["n_pairs"] == rt.n_pairs
         for key in ("token", "pos", "parent", "subtree_end", "node", "child_ptr", "child_idx",
-                    "q_ptr", "q_kb", "q_full", "kb_qhi", "fwd_order", "bwd_order"):
+                    "q_ptr", "q_kb", "q_full", "q_cls", "kb_qhi", "fwd_order", "bwd_order"):
             np.testing.assert_array_equal(e[key], getattr(rt, key), err_msg=key)
         assert e["seq_ids"].tolist() == rt.seq_ids
         assert e["seq_out_offsets"].tolist() == rt.out_offsets.tolist()

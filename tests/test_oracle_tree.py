@@ -172,16 +172,23 @@ def _check_invariants(seqs, cap, f):
             assert t.subtree_end[j] == np.nonzero(M[:, j])[0].max()
         # tile classes from a scan of the dense mask
         nb = Np // BLOCK
-        exp_ptr, exp_kb, exp_full = [0], [], []
+        exp_ptr, exp_kb, exp_full, exp_cls = [0], [], [], []
         for qb in range(nb):
             for kb in range(nb - 1, -1, -1):
                 blk = M[qb * BLOCK:(qb + 1) * BLOCK, kb * BLOCK:(kb + 1) * BLOCK]
                 if blk.any():
                     exp_kb.append(kb)
                     exp_full.append(int(blk.all()))
+                    bits = 0
+                    for qs in range(4):
+                        for ks in range(4):
+                            sub = blk[32 * qs:32 * qs + 32, 32 * ks:32 * ks + 32]
+                            bits |= (0 if not sub.any() else 2 if sub.all() else 1) << (2 * (4 * qs + ks))
+                    exp_cls.append(bits)
             exp_ptr.append(len(exp_kb))
         assert t.q_ptr.tolist() == exp_ptr
         assert t.q_kb.tolist() == exp_kb and t.q_full.tolist() == exp_full
+        assert t.q_cls.view(np.uint32).tolist() == exp_cls
         assert t.n_pairs == int(M[:N, :N].sum()) == int((t.pos[:N] + 1).sum())
         # child targets: every real token's distinct next tokens
         for i in range(N):
