@@ -81,54 +81,58 @@ def main():
     tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     d, hq, hkv = w.head_dim, w.hq, w.hkv
 
-    bufs = []
-    for t, s in enumerate(sizes):
-        Np = s["n_padded"]
-        b = {}
-        b["q"] = make_tensor((Np, hq, d), w.dtype, tree_tensor_seed(w.seed, t, "q"), dev)
-        b["k"] = make_tensor((Np, hkv, d), w.dtype, tree_tensor_seed(w.seed, t, "k"), dev)
-        b["v"] = make_tensor((Np, hkv, d), w.dtype, tree_tensor_seed(w.seed, t, "v"), dev)
-        b["o"] = torch.empty((Np, hq, d), dtype=tdt, device=dev)
-        b["lse"] = torch.empty((hq, Np), dtype=torch.float32, device=dev)
-        if w.bwd:
-            b["do"] = make_tensor((Np, hq, d), w.dtype, tree_tensor_seed(w.seed, t, "do"), dev)
-            b["dq"] = torch.empty_like(b["q"])
-            b["dk"] = torch.empty_like(b["k"])
-            b["dv"] = torch.empty_like(b["v"])
-            b["ws"] = torch.empty((hq, Np), dtype=torch.float32, device=dev)
-        if w.gather:
-            b["logits"] = make_tensor((Np, w.vocab), w.dtype, tree_tensor_seed(w.seed, t, "logits"),
-                                      dev, std=w.logit_std)
-            b["lp"] = torch.empty(s["n_out"], dtype=torch.float32, device=dev)
-            b["ent"] = torch.empty(s["n_out"], dtype=torch.float32, device=dev)
-        bufs.append(b)
+    # one buffer per tensor for the whole forest, trees back to back (the
+    # layout of the forest-level metadata); each tree's rows are drawn from
+    # their own seed
+    Np_all = sum(s["n_padded"] for s in sizes)
+    n_out_all = sum(s["n_out"] for s in sizes)
+
+    def forest_tensor(width_shape, name, std=1.0):
+        parts = [make_tensor((s["n_padded"],) + width_shape, w.dtype, tree_tensor_seed(w.seed, t, name),
+                             dev, std=std) for t, s in enumerate(sizes)]
+        out = torch.cat(parts) if len(parts) > 1 else parts[0]
+        del parts
+        return out.contiguous()
+
+    b = {}
+    b["q"] = forest_tensor((hq, d), "q")
+    b["k"] = forest_tensor((hkv, d), "k")
+    b["v"] = forest_tensor((hkv, d), "v")
+    b["o"] = torch.empty((Np_all, hq, d), dtype=tdt, device=dev)
+    b["lse"] = torch.empty((hq, Np_all), dtype=torch.float32, device=dev)
+    if w.bwd:
+        b["do"] = forest_tensor((hq, d), "do")
+        b["dq"] = torch.empty_like(b["q"])
+        b["dk"] = torch.empty_like(b["k"])
+        b["dv"] = torch.empty_like(b["v"])
+        b["ws"] = torch.empty((hq, Np_all), dtype=torch.float32, device=dev)
+    if w.gather:
+        b["logits"] = forest_tensor((w.vocab,), "logits", std=w.logit_std)
+        b["lp"] = torch.empty(n_out_all, dtype=torch.float32, device=dev)
+        b["ent"] = torch.empty(n_out_all, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def step(record):
         forest = pst.build_tree(w.seqs, w.max_tokens_per_mb)
-        metas = [pst.tree_meta_create(forest, t, stream) for t in range(forest.n_trees)]
-        evs = []
-        for t, m in enumerate(metas):
-            b = bufs[t]
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
-            if record:
-                e[0].record(stream)
-            pst.tree_attn_fwd(b["q"], b["k"], b["v"], m, out=b["o"], lse=b["lse"], stream=stream)
-            if record:
-                e[1].record(stream)
-            if w.bwd:
-                pst.tree_attn_bwd(b["q"], b["k"], b["v"], b["o"], b["lse"], b["do"], m,
-                                  dq=b["dq"], dk=b["dk"], dv=b["dv"], workspace=b["ws"], stream=stream)
-            if record:
-                e[2].record(stream)
-            if w.gather:
-                pst.gather_tree_logprobs_entropy(b["logits"], m, logprobs=b["lp"], entropy=b["ent"],
-                                                 stream=stream)
-            if record:
-                e[3].record(stream)
-            evs.append(e)
-        return forest, metas, evs
+        m = pst.forest_meta_create(forest, stream)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record(stream)
+        pst.tree_attn_fwd(b["q"], b["k"], b["v"], m, out=b["o"], lse=b["lse"], stream=stream)
+        if record:
+            e[1].record(stream)
+        if w.bwd:
+            pst.tree_attn_bwd(b["q"], b["k"], b["v"], b["o"], b["lse"], b["do"], m,
+                              dq=b["dq"], dk=b["dk"], dv=b["dv"], workspace=b["ws"], stream=stream)
+        if record:
+            e[2].record(stream)
+        if w.gather:
+            pst.gather_tree_logprobs_entropy(b["logits"], m, logprobs=b["lp"], entropy=b["ent"],
+                                             stream=stream)
+        if record:
+            e[3].record(stream)
+        return forest, [m], [e] if record else []
 
     def release(items):
         torch.cuda.synchronize()
@@ -172,19 +176,20 @@ def main():
     gat_t = sum(gat_ms) / K * 1e-3
     attn_tflops = (fwd_flops + bwd_flops) / (fwd_t + bwd_t) / 1e12
     kernels = {"attn_fwd": {"ms_per_step": fwd_t * 1e3, "TFLOP/s": fwd_flops / fwd_t / 1e12,
-                            "launches_per_step": n_trees}}
+                            "launches_per_step": 1}}
     if w.bwd:
         kernels["attn_bwd"] = {"ms_per_step": bwd_t * 1e3, "TFLOP/s": bwd_flops / bwd_t / 1e12,
-                               "launches_per_step": n_trees}
+                               "launches_per_step": 1}
     gather_bytes = 0
     if w.gather:
         esz = 4 if w.dtype == "f32" else 2
         n_out = sum(s["n_out"] for s in sizes)
         n_real = stats["tree_tokens"]
-        # logits of every real row once + two fp32 outputs and the row->output map
-        gather_bytes = n_real * w.vocab * esz + n_out * (4 + 4 + 4 + 4) + 4 * (n_real + n_trees)
+        # logits of every real row once + per output two fp32 writes and its
+        # slot and target reads + the row pointer of every row
+        gather_bytes = n_real * w.vocab * esz + n_out * (4 + 4 + 4 + 4) + 4 * (Np_all + 1)
         kernels["gather"] = {"ms_per_step": gat_t * 1e3, "GB/s": gather_bytes / gat_t / 1e9,
-                             "launches_per_step": n_trees}
+                             "launches_per_step": 1}
 
     # roofline of the kernel that takes the most time
     cands = [("attn_fwd", fwd_t), ("attn_bwd", bwd_t), ("gather", gat_t)]
@@ -193,13 +198,13 @@ def main():
         ach = gather_bytes / gat_t / 1e9
         roof = {"kernel": "gather", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS, "traffic": None,
-                "algorithmic_per_launch": gather_bytes / n_trees}
+                "algorithmic_per_launch": gather_bytes}
     else:
         fl, tt = (fwd_flops, fwd_t) if dom == "attn_fwd" else (bwd_flops, bwd_t)
         ach = fl / tt / 1e12
         peak = PEAK_TFLOPS[w.dtype]
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                "frac": ach / peak, "traffic": None, "algorithmic_per_launch": fl / n_trees}
+                "frac": ach / peak, "traffic": None, "algorithmic_per_launch": fl}
 
     out = {
         "metric": METRIC,
@@ -244,12 +249,12 @@ def main():
         del a, bcopy
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, sizes, bufs, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, sizes, b, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, sizes, bufs, target_s):
+def cpu_baseline(w, sizes, fb, target_s):
     """The oracle, as it stands, on a bounded sample of the same workload:
     the dense-mask float64 forward of tree 0 for as many query heads of the
     first key/value group as fit in about `target_s` seconds (at least one),
@@ -267,7 +272,9 @@ def cpu_baseline(w, sizes, bufs, target_s):
     ref = oracle.build_forest(w.seqs, w.max_tokens_per_mb)
     tree = ref.trees[0]
     G = w.hq // w.hkv
-    b = bufs[0]
+    # tree 0 occupies the first rows of the forest buffers
+    n0 = tree.n_padded
+    b = {key: fb[key][:n0] for key in ("q", "k", "v", "logits") if key in fb}
     h64 = lambda x: x.detach().to("cpu", torch.float64).numpy()  # noqa: E731
     mask = oracle.dense_mask(tree)
     # whole key/value groups of query heads (group g serves heads g*G .. g*G+G-1)

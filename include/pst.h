@@ -158,6 +158,13 @@ void pst_forest_free(pst_forest* forest);
  * Errors: PST_EINVAL, PST_ERANGE, PST_ENOMEM, PST_EHIP. */
 int pst_tree_meta_create(const pst_forest* forest, int32_t tree, void* stream,
                          pst_tree_meta** out);
+/* The metadata of every tree of the forest at once, trees back to back in
+ * tree order: the padded rows of tree t follow those of trees 0..t-1, and
+ * its outputs (logprobs/entropy) follow theirs.  Attention never crosses
+ * trees, so one call of the device entry points below then covers the whole
+ * forest, with tensors of sum-over-trees Np rows.  Same errors as
+ * pst_tree_meta_create; sizes (pst_tree_meta_sizes) are sums over trees. */
+int pst_forest_meta_create(const pst_forest* forest, void* stream, pst_tree_meta** out);
 int pst_tree_meta_sizes(const pst_tree_meta* meta, pst_tree_sizes* out);
 /* Frees the metadata.  The caller first makes sure no work that reads it is
  * still queued (synchronize the stream it was used on). */

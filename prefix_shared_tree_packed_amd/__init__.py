@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     TreeMeta,
     build_tree,
     tree_meta_create,
+    forest_meta_create,
     tree_attn_fwd,
     tree_attn_bwd,
     tree_attn_bwd_workspace_bytes,

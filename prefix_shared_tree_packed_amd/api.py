@@ -122,10 +122,15 @@ def build_tree(seqs: Sequence, max_tokens_per_mb: int) -> Forest:
 class TreeMeta:
     """Device-resident metadata of one tree (pst_tree_meta)."""
 
-    def __init__(self, forest: Forest, tree: int, stream=None):
+    def __init__(self, forest: Forest, tree: Optional[int], stream=None):
+        """tree=None: the whole forest, trees back to back (pst_forest_meta_create)."""
         h = c_void_p()
         self._h = None
-        check(_lib.load().pst_tree_meta_create(forest._h, int(tree), c_void_p(_stream_ptr(stream)), byref(h)))
+        lib = _lib.load()
+        if tree is None:
+            check(lib.pst_forest_meta_create(forest._h, c_void_p(_stream_ptr(stream)), byref(h)))
+        else:
+            check(lib.pst_tree_meta_create(forest._h, int(tree), c_void_p(_stream_ptr(stream)), byref(h)))
         self._h = h
         s = _lib.TreeSizes()
         check(_lib.load().pst_tree_meta_sizes(self._h, byref(s)))
@@ -153,6 +158,10 @@ class TreeMeta:
 
 def tree_meta_create(forest: Forest, tree: int, stream=None) -> TreeMeta:
     return TreeMeta(forest, tree, stream)
+
+
+def forest_meta_create(forest: Forest, stream=None) -> TreeMeta:
+    return TreeMeta(forest, None, stream)
 
 
 def tree_attn_fwd(q, k, v, meta: TreeMeta, softmax_scale: Optional[float] = None,
@@ -212,8 +221,8 @@ def tree_attn_bwd(q, k, v, o, lse, dout, meta: TreeMeta, softmax_scale: Optional
 def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=None, stream=None):
     import torch
     _dev_tensor(logits, "logits")
-    if logits.dim() != 2 or logits.shape[0] < meta.n_tokens:
-        raise ValueError(f"logits must be [>= {meta.n_tokens}, V], got {tuple(logits.shape)}")
+    if logits.dim() != 2 or logits.shape[0] != meta.n_padded:
+        raise ValueError(f"logits must be [{meta.n_padded}, V], got {tuple(logits.shape)}")
     n = meta.n_out
     if logprobs is None:
         logprobs = torch.empty(n, dtype=torch.float32, device=logits.device)

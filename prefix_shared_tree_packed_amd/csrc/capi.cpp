@@ -7,6 +7,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <numeric>
+#include <vector>
 #include <new>
 #include <string>
 
@@ -19,7 +21,7 @@ struct pst_forest {
 
 // Device layout of one tree's metadata: a single int32 allocation holding
 // se [Np] | q_ptr [nb+1] | q_tile [n_tiles] | kb_qhi [nb] | fwd_order [nb] |
-// bwd_order [nb] | row_out_ptr [N+1] | out_pos [n_out] | out_tgt [n_out] |
+// bwd_order [nb] | row_out_ptr [Np+1] | out_pos [n_out] | out_tgt [n_out] |
 // blk32 [Np/32][2] (min, max subtree end of each 32-key block) |
 // q_cls [n_tiles] (32x32 sub-block classes of each tile), every
 // section starting on a 16-byte boundary.  The pinned staging copy is
@@ -119,6 +121,137 @@ int check_ptrs(std::initializer_list<const void*> ps, const char* names) {
 
 float resolve_scale(float s, int32_t head_dim) {
   return s > 0.f ? s : 1.0f / std::sqrt(static_cast<float>(head_dim));
+}
+
+// Uploads the metadata of `trees`, laid back to back in the given order:
+// rows of tree t follow the padded rows of the trees before it, its outputs
+// follow theirs.  Attention never crosses trees, so the concatenation is
+// itself a valid packed layout and one launch serves all of them.
+int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tree_meta** out) {
+  int64_t Np = 0, nb = 0, n_tiles = 0, n_out = 0;
+  pst_tree_sizes sz{};
+  for (const pst::Tree* t : trees) {
+    pst_tree_sizes ts{};
+    fill_sizes(*t, &ts);
+    Np += t->Np;
+    nb += t->nb;
+    n_tiles += t->n_tiles();
+    n_out += t->n_out();
+    sz.n_tokens += ts.n_tokens;
+    sz.n_nodes += ts.n_nodes;
+    sz.n_seqs += ts.n_seqs;
+    sz.n_edges += ts.n_edges;
+    sz.n_node_seq += ts.n_node_seq;
+    sz.n_pairs += ts.n_pairs;
+  }
+  if (Np >= (int64_t{1} << 30) || n_out >= (int64_t{1} << 31) || n_tiles >= (int64_t{1} << 31))
+    return fail(PST_EINVAL, "forest too large for 32-bit row, tile or output indices");
+  sz.n_padded = static_cast<int32_t>(Np);
+  sz.n_blocks = static_cast<int32_t>(nb);
+  sz.n_tiles = static_cast<int32_t>(n_tiles);
+  sz.n_out = n_out;
+
+  auto round4 = [](int64_t n) { return static_cast<size_t>((n + 3) / 4 * 4); };
+  size_t off = 0;
+  const size_t o_se = off;        off += round4(Np);
+  const size_t o_qptr = off;      off += round4(nb + 1);
+  const size_t o_qtile = off;     off += round4(n_tiles);
+  const size_t o_qhi = off;       off += round4(nb);
+  const size_t o_ford = off;      off += round4(nb);
+  const size_t o_bord = off;      off += round4(nb);
+  const size_t o_rptr = off;      off += round4(Np + 1);
+  const size_t o_opos = off;      off += round4(n_out);
+  const size_t o_otgt = off;      off += round4(n_out);
+  const size_t o_blk = off;       off += round4(Np / 16);
+  const size_t o_qcls = off;      off += round4(n_tiles);
+  const size_t words = off;
+
+  pst_tree_meta* m = new (std::nothrow) pst_tree_meta;
+  if (!m) return fail(PST_ENOMEM, "out of host memory");
+  hipError_t e = hipGetDevice(&m->device);
+  if (e != hipSuccess) {
+    delete m;
+    return hip_fail(e, "hipGetDevice");
+  }
+  e = hipHostMalloc(reinterpret_cast<void**>(&m->hbuf), words * sizeof(int32_t), hipHostMallocDefault);
+  if (e != hipSuccess) {
+    delete m;
+    return fail(PST_ENOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  }
+  e = hipMalloc(reinterpret_cast<void**>(&m->dbuf), words * sizeof(int32_t));
+  if (e != hipSuccess) {
+    (void)hipHostFree(m->hbuf);
+    delete m;
+    return fail(PST_ENOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+  }
+  int32_t* h = m->hbuf;
+  std::memset(h, 0, words * sizeof(int32_t));
+  int32_t row0 = 0, blk0 = 0, tile0 = 0, out0 = 0;
+  bool any_target = false;
+  for (const pst::Tree* tp : trees) {
+    const pst::Tree& t = *tp;
+    for (int32_t i = 0; i < t.Np; ++i) h[o_se + row0 + i] = t.se[i] + row0;
+    for (int32_t qb = 0; qb < t.nb; ++qb) h[o_qptr + blk0 + qb] = tile0 + t.q_ptr[qb];
+    for (int32_t i = 0; i < t.n_tiles(); ++i) {
+      h[o_qtile + tile0 + i] = ((t.q_kb[i] + blk0) << 1) | (t.q_full[i] & 1);
+      h[o_qcls + tile0 + i] = t.q_cls[i];
+    }
+    for (int32_t kb = 0; kb < t.nb; ++kb) h[o_qhi + blk0 + kb] = t.kb_qhi[kb] + blk0;
+    for (int32_t r = 0; r < t.Np; ++r)
+      h[o_rptr + row0 + r] = out0 + (r < t.N ? t.row_out_ptr[r] : static_cast<int32_t>(t.n_out()));
+    for (int64_t o = 0; o < t.n_out(); ++o) {
+      h[o_opos + out0 + o] = out0 + t.out_pos[o];
+      h[o_otgt + out0 + o] = t.out_tgt[o];
+    }
+    if (t.max_target >= 0) {
+      m->min_target = any_target ? std::min(m->min_target, t.min_target) : t.min_target;
+      m->max_target = any_target ? std::max(m->max_target, t.max_target) : t.max_target;
+      any_target = true;
+    }
+    row0 += t.Np;
+    blk0 += t.nb;
+    tile0 += t.n_tiles();
+    out0 += static_cast<int32_t>(t.n_out());
+  }
+  h[o_qptr + nb] = tile0;
+  h[o_rptr + Np] = out0;
+  for (int64_t b = 0; b < Np / 32; ++b) {
+    const int32_t* se = h + o_se + 32 * b;
+    h[o_blk + 2 * b] = *std::min_element(se, se + 32);
+    h[o_blk + 2 * b + 1] = *std::max_element(se, se + 32);
+  }
+  // longest-processing-time orders over every block of every tree
+  {
+    std::vector<int32_t> ord(nb);
+    std::iota(ord.begin(), ord.end(), 0);
+    const int32_t* qp = h + o_qptr;
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
+      return qp[a + 1] - qp[a] > qp[b + 1] - qp[b];
+    });
+    std::copy(ord.begin(), ord.end(), h + o_ford);
+    std::iota(ord.begin(), ord.end(), 0);
+    const int32_t* qhi = h + o_qhi;
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
+      return qhi[a] - a > qhi[b] - b;
+    });
+    std::copy(ord.begin(), ord.end(), h + o_bord);
+  }
+  e = hipMemcpyAsync(m->dbuf, h, words * sizeof(int32_t), hipMemcpyHostToDevice,
+                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipFree(m->dbuf);
+    (void)hipHostFree(m->hbuf);
+    delete m;
+    return hip_fail(e, "hipMemcpyAsync");
+  }
+  m->n_words = words;
+  m->sizes = sz;
+  int32_t* d = m->dbuf;
+  m->dev = pst::TreeDev{d + o_se,   d + o_qptr, d + o_qtile, d + o_qhi,  d + o_ford,
+                        d + o_bord, d + o_rptr, d + o_opos,  d + o_otgt, d + o_blk, d + o_qcls,
+                        sz.n_tokens, sz.n_padded, sz.n_blocks, sz.n_tiles};
+  *out = m;
+  return ok();
 }
 
 }  // namespace
@@ -228,84 +361,16 @@ int pst_tree_meta_create(const pst_forest* forest, int32_t tree, void* stream,
   if (!out) return fail(PST_EINVAL, "out is NULL");
   *out = nullptr;
   if (int e = check_tree(forest, tree)) return e;
-  const pst::Tree& t = forest->f.trees[tree];
+  return create_meta({&forest->f.trees[tree]}, stream, out);
+}
 
-  auto round4 = [](size_t n) { return (n + 3) / 4 * 4; };
-  const size_t n_tiles = t.q_kb.size();
-  const size_t n_out = static_cast<size_t>(t.n_out());
-  size_t off = 0;
-  const size_t o_se = off;        off += round4(t.Np);
-  const size_t o_qptr = off;      off += round4(t.nb + 1);
-  const size_t o_qtile = off;     off += round4(n_tiles);
-  const size_t o_qhi = off;       off += round4(t.nb);
-  const size_t o_ford = off;      off += round4(t.nb);
-  const size_t o_bord = off;      off += round4(t.nb);
-  const size_t o_rptr = off;      off += round4(static_cast<size_t>(t.N) + 1);
-  const size_t o_opos = off;      off += round4(n_out);
-  const size_t o_otgt = off;      off += round4(n_out);
-  const size_t o_blk = off;       off += round4(static_cast<size_t>(t.Np) / 16);
-  const size_t o_qcls = off;      off += round4(n_tiles);
-  const size_t words = off;
-
-  pst_tree_meta* m = new (std::nothrow) pst_tree_meta;
-  if (!m) return fail(PST_ENOMEM, "out of host memory");
-  hipError_t e = hipGetDevice(&m->device);
-  if (e != hipSuccess) {
-    delete m;
-    return hip_fail(e, "hipGetDevice");
-  }
-  e = hipHostMalloc(reinterpret_cast<void**>(&m->hbuf), words * sizeof(int32_t), hipHostMallocDefault);
-  if (e != hipSuccess) {
-    delete m;
-    return fail(PST_ENOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
-  }
-  e = hipMalloc(reinterpret_cast<void**>(&m->dbuf), words * sizeof(int32_t));
-  if (e != hipSuccess) {
-    (void)hipHostFree(m->hbuf);
-    delete m;
-    return fail(PST_ENOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
-  }
-  int32_t* h = m->hbuf;
-  std::memset(h, 0, words * sizeof(int32_t));
-  std::memcpy(h + o_se, t.se.data(), t.se.size() * 4);
-  std::memcpy(h + o_qptr, t.q_ptr.data(), t.q_ptr.size() * 4);
-  for (size_t i = 0; i < n_tiles; ++i) h[o_qtile + i] = (t.q_kb[i] << 1) | (t.q_full[i] & 1);
-  std::memcpy(h + o_qhi, t.kb_qhi.data(), t.kb_qhi.size() * 4);
-  std::memcpy(h + o_ford, t.fwd_order.data(), t.fwd_order.size() * 4);
-  std::memcpy(h + o_bord, t.bwd_order.data(), t.bwd_order.size() * 4);
-  std::memcpy(h + o_rptr, t.row_out_ptr.data(), t.row_out_ptr.size() * 4);
-  if (n_out) {
-    std::memcpy(h + o_opos, t.out_pos.data(), n_out * 4);
-    std::memcpy(h + o_otgt, t.out_tgt.data(), n_out * 4);
-  }
-  if (n_tiles) std::memcpy(h + o_qcls, t.q_cls.data(), n_tiles * 4);
-  for (int32_t b = 0; b < t.Np / 32; ++b) {
-    int32_t lo = t.se[32 * b], hi = t.se[32 * b];
-    for (int32_t j = 32 * b + 1; j < 32 * b + 32; ++j) {
-      lo = std::min(lo, t.se[j]);
-      hi = std::max(hi, t.se[j]);
-    }
-    h[o_blk + 2 * b] = lo;
-    h[o_blk + 2 * b + 1] = hi;
-  }
-  e = hipMemcpyAsync(m->dbuf, h, words * sizeof(int32_t), hipMemcpyHostToDevice,
-                     static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    (void)hipFree(m->dbuf);
-    (void)hipHostFree(m->hbuf);
-    delete m;
-    return hip_fail(e, "hipMemcpyAsync");
-  }
-  m->n_words = words;
-  fill_sizes(t, &m->sizes);
-  int32_t* d = m->dbuf;
-  m->dev = pst::TreeDev{d + o_se,   d + o_qptr, d + o_qtile, d + o_qhi,  d + o_ford,
-                        d + o_bord, d + o_rptr, d + o_opos,  d + o_otgt, d + o_blk, d + o_qcls,
-                        t.N,        t.Np,       t.nb,        static_cast<int32_t>(n_tiles)};
-  m->min_target = t.min_target;
-  m->max_target = t.max_target;
-  *out = m;
-  return ok();
+int pst_forest_meta_create(const pst_forest* forest, void* stream, pst_tree_meta** out) {
+  if (!out) return fail(PST_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!forest) return fail(PST_EINVAL, "forest is NULL");
+  std::vector<const pst::Tree*> trees;
+  for (const pst::Tree& t : forest->f.trees) trees.push_back(&t);
+  return create_meta(trees, stream, out);
 }
 
 int pst_tree_meta_sizes(const pst_tree_meta* meta, pst_tree_sizes* out) {

@@ -29,7 +29,7 @@ struct TreeDev {
   const int32_t* kb_qhi;       // [nb] last query block seeing each key block
   const int32_t* fwd_order;    // [nb] query blocks, heaviest first
   const int32_t* bwd_order;    // [nb] key blocks, heaviest first
-  const int32_t* row_out_ptr;  // [N+1] outputs of each real row
+  const int32_t* row_out_ptr;  // [Np+1] outputs of each row (none for pad rows)
   const int32_t* out_pos;      // [n_out] output slot
   const int32_t* out_tgt;      // [n_out] next-token id, -1 for a last token
   const int32_t* blk32;        // [Np/32][2] min and max subtree end of each 32-key block

@@ -11,7 +11,7 @@
 // different next tokens.  The host's row_out_ptr / out_pos / out_tgt map
 // lists those outputs per row.
 //
-// One 256-thread workgroup per real row.  Each thread streams 16-byte chunks
+// One 256-thread workgroup per row; pad rows (no outputs) return at once.  Each thread streams 16-byte chunks
 // (four in flight) and keeps an online (max, sum e^(x-max), sum e^(x-max)*x)
 // triple; triples merge across the wave with butterfly shuffles and across
 // the four waves through LDS.  Pad rows are never read.  The kernel is
@@ -87,7 +87,7 @@ __device__ __forceinline__ void unpack<float>(const uint4& u, float (&x)[4]) {
 }
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;  // 16-byte chunks in flight per thread
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ logits, int64_t V,
@@ -99,6 +99,9 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
 
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int o_begin = tr.row_out_ptr[row];
+  const int o_end = tr.row_out_ptr[row + 1];
+  if (o_begin == o_end) return;  // a pad row: nothing reads it
   const T* x = logits + static_cast<size_t>(row) * V;
 
   // aligned body in 16-byte chunks, unaligned head/tail element by element
@@ -116,12 +119,16 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
     u32x4_t u[kUnroll];
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) u[j] = __builtin_nontemporal_load(body + ch + j * kThreads);
+    // one max and one rescale per batch, then the exponentials
+    float f[kUnroll * EPC];
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
-      float f[EPC];
-      unpack<T>(uint4{u[j].x, u[j].y, u[j].z, u[j].w}, f);
-      absorb(a, f);
+      float g[EPC];
+      unpack<T>(uint4{u[j].x, u[j].y, u[j].z, u[j].w}, g);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) f[j * EPC + e] = g[e];
     }
+    absorb(a, f);
   }
   for (; ch < nch; ch += kThreads) {
     float f[EPC];
@@ -156,8 +163,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
   __syncthreads();
   const float lse = row_stats[0];
   const float ent = row_stats[1];
-  const int o_end = tr.row_out_ptr[row + 1];
-  for (int k = tr.row_out_ptr[row] + tid; k < o_end; k += kThreads) {
+  for (int k = o_begin + tid; k < o_end; k += kThreads) {
     const int slot = tr.out_pos[k];
     const int tgt = tr.out_tgt[k];
     entropy[slot] = ent;
@@ -169,8 +175,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
 
 hipError_t launch_gather(int dtype, const void* logits, int64_t vocab, const TreeDev& tr,
                          float* logprobs, float* entropy, hipStream_t stream) {
-  if (tr.N == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(tr.N));
+  if (tr.Np == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tr.Np));  // pad rows exit at once
   if (dtype == kDtypeBf16)
     hipLaunchKernelGGL(gather_kernel<bf16_t>, grid, dim3(kThreads), 0, stream,
                        static_cast<const bf16_t*>(logits), vocab, tr, logprobs, entropy);

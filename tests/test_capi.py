@@ -41,6 +41,13 @@ def test_meta_create_rejects_bad_tree_index():
         assert not out.value
 
 
+def test_forest_meta_rejects_null_forest():
+    lib = pst.load()
+    out = ctypes.c_void_p()
+    assert _lib.ERRORS[lib.pst_forest_meta_create(None, None, ctypes.byref(out))] == "PST_EINVAL"
+    assert _lib.ERRORS[lib.pst_forest_meta_create(None, None, None)] == "PST_EINVAL"
+
+
 def test_null_arguments():
     lib = pst.load()
     out = ctypes.c_void_p()

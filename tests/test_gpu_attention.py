@@ -212,3 +212,34 @@ def test_invalid_shapes_rejected(gpu_lib):
         torch.cuda.synchronize()
     finally:
         case.close()
+
+
+def test_forest_meta_matches_per_tree(gpu_lib):
+    """One launch over the whole forest (trees back to back) gives bitwise
+    the same outputs and gradients as one launch per tree."""
+    import torch
+    rng = np.random.default_rng(21)
+    seqs = prompt_groups(rng, 5, 200, 3, 30, 300)
+    case = Case(seqs, 512)
+    try:
+        assert len(case.ref.trees) >= 3
+        fmeta = gpu_lib.forest_meta_create(case.forest)
+        Np = sum(t.n_padded for t in case.ref.trees)
+        assert fmeta.n_padded == Np
+        q, k, v, do = attn_inputs(Np, 8, 2, 128, "bf16", 60, with_dout=True)
+        o, lse = gpu_lib.tree_attn_fwd(q, k, v, fmeta)
+        dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, fmeta)
+        r0 = 0
+        for t, tree in enumerate(case.ref.trees):
+            sl = slice(r0, r0 + tree.n_padded)
+            qs, ks, vs, dos = (x[sl].contiguous() for x in (q, k, v, do))
+            ot, lt = gpu_lib.tree_attn_fwd(qs, ks, vs, case.metas[t])
+            dqt, dkt, dvt = gpu_lib.tree_attn_bwd(qs, ks, vs, ot, lt, dos, case.metas[t])
+            torch.cuda.synchronize()
+            assert torch.equal(o[sl], ot) and torch.equal(lse[:, sl], lt)
+            assert torch.equal(dq[sl], dqt) and torch.equal(dk[sl], dkt) and torch.equal(dv[sl], dvt)
+            r0 += tree.n_padded
+        torch.cuda.synchronize()
+        fmeta.destroy()
+    finally:
+        case.close()

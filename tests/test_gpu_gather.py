@@ -101,3 +101,29 @@ def test_gather_rejects_out_of_vocab(gpu_lib):
         assert e.value.name == "PST_EINVAL"
     finally:
         case.close()
+
+
+def test_gather_forest_meta_matches_per_tree(gpu_lib):
+    import torch
+    rng = np.random.default_rng(8)
+    seqs = prompt_groups(rng, 5, 120, 3, 10, 200, vocab=1000)
+    case = Case(seqs, 384)
+    try:
+        fmeta = gpu_lib.forest_meta_create(case.forest)
+        Np = sum(t.n_padded for t in case.ref.trees)
+        logits = make_tensor((Np, 1001), "bf16", 77, "cuda", std=2.0)
+        lp, ent = gpu_lib.gather_tree_logprobs_entropy(logits, fmeta)
+        r0, o0 = 0, 0
+        for t, tree in enumerate(case.ref.trees):
+            lpt, entt = gpu_lib.gather_tree_logprobs_entropy(
+                logits[r0:r0 + tree.n_padded].contiguous(), case.metas[t])
+            n = int(tree.out_offsets[-1])
+            torch.cuda.synchronize()
+            assert torch.equal(lp[o0:o0 + n], lpt) and torch.equal(ent[o0:o0 + n], entt)
+            r0 += tree.n_padded
+            o0 += n
+        assert o0 == lp.numel()
+        torch.cuda.synchronize()
+        fmeta.destroy()
+    finally:
+        case.close()
