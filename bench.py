@@ -105,7 +105,11 @@ def main():
         b["dq"] = torch.empty_like(b["q"])
         b["dk"] = torch.empty_like(b["k"])
         b["dv"] = torch.empty_like(b["v"])
-        b["ws"] = torch.empty((hq, Np_all), dtype=torch.float32, device=dev)
+        shape_meta = pst.forest_meta_create(shape_forest)
+        ws_bytes = pst.tree_attn_bwd_workspace_bytes(shape_meta, hq, hkv, d, w.dtype)
+        torch.cuda.synchronize()
+        shape_meta.destroy()
+        b["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if w.gather:
         b["logits"] = forest_tensor((w.vocab,), "logits", std=w.logit_std)
         b["lp"] = torch.empty(n_out_all, dtype=torch.float32, device=dev)

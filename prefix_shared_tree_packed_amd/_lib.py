@@ -66,7 +66,8 @@ _SIGS = {
     "pst_tree_meta_destroy": (c_int32, [c_void_p]),
     "pst_tree_attn_fwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_int32, c_int32, c_int32, c_int32, c_float, c_void_p]),
-    "pst_tree_attn_bwd_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_size_t)]),
+    "pst_tree_attn_bwd_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                                     POINTER(c_size_t)]),
     "pst_tree_attn_bwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
                                     c_int32, c_int32, c_int32, c_int32, c_float, c_void_p]),

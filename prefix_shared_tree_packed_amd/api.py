@@ -187,9 +187,12 @@ def tree_attn_fwd(q, k, v, meta: TreeMeta, softmax_scale: Optional[float] = None
     return out, lse
 
 
-def tree_attn_bwd_workspace_bytes(meta: TreeMeta, hq: int, head_dim: int) -> int:
+def tree_attn_bwd_workspace_bytes(meta: TreeMeta, hq: int, hkv: int, head_dim: int,
+                                  dtype: str) -> int:
+    """Device workspace bytes of tree_attn_bwd for these shapes; dtype "f32" or "bf16"."""
     n = c_size_t()
-    check(_lib.load().pst_tree_attn_bwd_workspace_bytes(meta._h, hq, head_dim, byref(n)))
+    code = {"f32": 0, "bf16": 1}[dtype]
+    check(_lib.load().pst_tree_attn_bwd_workspace_bytes(meta._h, hq, hkv, head_dim, code, byref(n)))
     return n.value
 
 
@@ -206,9 +209,10 @@ def tree_attn_bwd(q, k, v, o, lse, dout, meta: TreeMeta, softmax_scale: Optional
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    nbytes = tree_attn_bwd_workspace_bytes(meta, hq, d)
+    nbytes = tree_attn_bwd_workspace_bytes(meta, hq, hkv, d,
+                                           "bf16" if q.dtype == torch.bfloat16 else "f32")
     if workspace is None:
-        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     check(_lib.load().pst_tree_attn_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
         _dev_tensor(dq, "dq").data_ptr(), _dev_tensor(dk, "dk").data_ptr(),

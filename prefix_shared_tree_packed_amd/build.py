@@ -37,6 +37,7 @@ HIP_SOURCES = [
     "kernels/attn_fwd.hip",
     "kernels/attn_fwd_bf16.hip",
     "kernels/attn_bwd.hip",
+    "kernels/attn_bwd_bf16.hip",
     "kernels/gather.hip",
 ]
 CXX_SOURCES = ["host/forest.cpp"]

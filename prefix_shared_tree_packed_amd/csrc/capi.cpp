@@ -402,12 +402,18 @@ int pst_tree_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
   return ok();
 }
 
-int pst_tree_attn_bwd_workspace_bytes(const pst_tree_meta* meta, int32_t hq, int32_t head_dim,
-                                      size_t* bytes) {
-  (void)head_dim;
-  if (!meta || !bytes) return fail(PST_EINVAL, "NULL argument");
-  if (hq <= 0) return fail(PST_ESHAPE, "hq must be positive");
-  *bytes = static_cast<size_t>(meta->sizes.n_padded) * hq * sizeof(float);
+static size_t bwd_workspace_bytes(const pst_tree_meta* meta, int hq, int hkv, int head_dim,
+                                  int dtype) {
+  const int Np = meta->sizes.n_padded;
+  if (dtype == PST_BF16 && head_dim == 128) return pst::attn_bwd_bf16_d128_workspace(Np, hq, hkv);
+  return static_cast<size_t>(Np) * hq * sizeof(float);
+}
+
+int pst_tree_attn_bwd_workspace_bytes(const pst_tree_meta* meta, int32_t hq, int32_t hkv,
+                                      int32_t head_dim, int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(PST_EINVAL, "NULL argument");
+  if (int e = check_attn_args(meta, hq, hkv, head_dim, dtype)) return e;
+  *bytes = bwd_workspace_bytes(meta, hq, hkv, head_dim, dtype);
   return ok();
 }
 
@@ -420,13 +426,13 @@ int pst_tree_attn_bwd(const void* q, const void* k, const void* v, const void* o
   if (int e = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv, workspace},
                          "q, k, v, o, lse, dout, dq, dk, dv, workspace"))
     return e;
-  const size_t need = static_cast<size_t>(meta->sizes.n_padded) * hq * sizeof(float);
+  const size_t need = bwd_workspace_bytes(meta, hq, hkv, head_dim, dtype);
   if (workspace_bytes < need)
     return fail(PST_EINVAL, "workspace of " + std::to_string(workspace_bytes) + " bytes < " +
                                 std::to_string(need) + " needed");
   if (int e = check_meta_device(meta)) return e;
   const hipError_t e = pst::launch_attn_bwd(
-      dtype, head_dim, q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace),
+      dtype, head_dim, q, k, v, o, lse, dout, dq, dk, dv, workspace,
       meta->dev, hq, hkv, resolve_scale(softmax_scale, head_dim), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tree_attn_bwd launch");
   return ok();

@@ -372,11 +372,13 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
 
 hipError_t launch_attn_bwd(int dtype, int head_dim, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                           void* dv, float* ws, const TreeDev& tr, int hq, int hkv, float scale,
-                           hipStream_t stream) {
+                           void* dv, void* workspace, const TreeDev& tr, int hq, int hkv,
+                           float scale, hipStream_t stream) {
+  float* ws = static_cast<float*>(workspace);
   if (dtype == kDtypeBf16) {
     if (head_dim == 128)
-      return launch<bf16_t, 128>(q, k, v, o, lse, dout, dq, dk, dv, ws, tr, hq, hkv, scale, stream);
+      return launch_attn_bwd_bf16_d128(q, k, v, o, lse, dout, dq, dk, dv, workspace, tr, hq, hkv,
+                                       scale, stream);
     if (head_dim == 64)
       return launch<bf16_t, 64>(q, k, v, o, lse, dout, dq, dk, dv, ws, tr, hq, hkv, scale, stream);
   } else {

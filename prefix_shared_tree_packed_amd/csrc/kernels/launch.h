@@ -25,11 +25,21 @@ hipError_t launch_attn_fwd_bf16_d128(const void* q, const void* k, const void* v
                                      float* lse, const TreeDev& tr, int hq, int hkv, float scale,
                                      hipStream_t stream);
 
-// workspace: float32 [hq, Np] (the per-row dO.O sums).
+// workspace: float32 [hq, Np] (the per-row dO.O sums); for bf16 / head_dim
+// 128 followed by the transposed tiles of attn_bwd_bf16.hip, in all
+// attn_bwd_bf16_d128_workspace bytes.
 hipError_t launch_attn_bwd(int dtype, int head_dim, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                           void* dv, float* workspace, const TreeDev& tr, int hq, int hkv,
+                           void* dv, void* workspace, const TreeDev& tr, int hq, int hkv,
                            float scale, hipStream_t stream);
+
+// bf16 / head_dim 128 performance kernels (attn_bwd_bf16.hip), reached
+// through launch_attn_bwd.
+size_t attn_bwd_bf16_d128_workspace(int Np, int hq, int hkv);
+hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v, const void* o,
+                                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                     void* workspace, const TreeDev& tr, int hq, int hkv, float scale,
+                                     hipStream_t stream);
 
 hipError_t launch_gather(int dtype, const void* logits, int64_t vocab, const TreeDev& tr,
                          float* logprobs, float* entropy, hipStream_t stream);

@@ -133,7 +133,7 @@ def test_bwd_worked_example(gpu_lib):
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("f32", 4, 2, 64), ("bf16", 8, 2, 128),
-                                             ("bf16", 5, 1, 64)])
+                                             ("bf16", 5, 1, 64), ("bf16", 6, 6, 128)])
 def test_bwd_several_tiles(gpu_lib, dtype, hq, hkv, d):
     rng = np.random.default_rng(hq * 13 + d)
     seqs = prompt_groups(rng, 3, 150, 3, 20, 260)
