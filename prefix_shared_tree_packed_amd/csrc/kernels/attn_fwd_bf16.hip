@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
         }
       }
-      mx = fmaxf(mx, swap_halves(mx));
+      mx = max_halves(mx);
       const float mxc = mx * c;
       if (__any(mxc > m_used + kRescale)) {
         const float m_new = fmaxf(m_used, mxc);
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
           }
         }
       }
-      sum += swap_halves(sum);
+      sum = sum_halves(sum);
       l += sum;
 
       // O^T += V^T.P^T

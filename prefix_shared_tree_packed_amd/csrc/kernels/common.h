@@ -58,6 +58,25 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Value of lane (lane ^ 32): swaps the two halves of the wave.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// Both halves' values at every lane: {x[l % 32], x[32 + l % 32]} for lane l,
+// by one v_permlane32_swap (a VALU op; a shuffle through ds_bpermute costs an
+// LDS round trip).
+__device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float a, b;
+  half_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a, b;
+  half_pair(x, a, b);
+  return a + b;
+}
+
 // Linear workgroup id -> logical work id such that consecutive logical ids
 // land on the same XCD.  Workgroups are dispatched round-robin over the 8
 // XCDs, so XCD x receives linear ids x, x+8, x+16, ...; those become the
