@@ -10,9 +10,14 @@
 //    16 (token 16t+8a+4h+j sits at 16t+8h+4a+j).  A contraction over tokens
 //    then reads each MFMA operand as ONE 16-byte LDS load, and every tile --
 //    row-major or transposed -- reaches LDS by global_load_lds_dwordx4 (no
-//    VGPRs, no VALU), 64 tokens per step through two named buffers.
+//    VGPRs, no VALU) through two named buffers: 64 queries per step in the
+//    dK/dV kernel (one workgroup per CU, 129 KB), 32 keys per step in the dQ
+//    kernel (49 KB, two workgroups per CU, which measured 1.5x faster than
+//    one; the dK/dV kernel at 32 does not fit two waves per SIMD without
+//    spilling and measured slower).
 //  * Row-major LDS tiles store 16-byte chunk c of row r at c ^ (r & 15);
-//    transposed half-tiles (128-byte rows) store it at c ^ ((d >> 1) & 7).
+//    transposed half-tiles (128-byte rows) store it at c ^ ((d >> 1) & 7),
+//    transposed 32-token slices (64-byte rows) at c ^ ((d >> 2) & 3).
 //  * Work per (wave, 32x32 sub-block) is skipped when no pair is visible and
 //    masked element by element only when some are: (unsigned)(i - j) <=
 //    se[j] - j.
@@ -149,6 +154,38 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(
     *reinterpret_cast<uint4*>(a_dst + d * kTile + 8 * c) = make_uint4(wa[0], wa[1], wa[2], wa[3]);
     if (qitem)
       *reinterpret_cast<uint4*>(b_dst + d * kTile + 8 * c) = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+  }
+}
+
+// The dQ kernel streams 32 keys per pipeline step (8 KB per tile), so that
+// two workgroups share a CU and two waves share each SIMD.
+constexpr int kQStep = 32;
+constexpr int kQBuf = kQStep * kRowB;  // 8 KB
+constexpr int kQTRowB = kQStep * 2;    // transposed slice row: 64 bytes
+
+// Transposed slice: 128 rows (d) of 64 bytes (32 permuted positions) at `src`
+// (row stride 256 bytes in the workspace tile) -> LDS, chunk c of row d at
+// c ^ ((d >> 2) & 3); two DMA instructions per wave.
+__device__ __forceinline__ void dma_trows32(const char* src, uint8_t* dst, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int d = 16 * (2 * wave + i) + (lane >> 2);
+    const int cch = (lane & 3) ^ ((d >> 2) & 3);
+    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(d) * kRowB + (cch << 4),
+                                     (lds_void*)(dst + (2 * wave + i) * 1024), 16, 0, 0);
+  }
+}
+
+// Row-major slice: 32 rows of 256 bytes (row stride `stride`) -> LDS, chunk
+// c of row r at c ^ (r & 15); two DMA instructions per wave.
+__device__ __forceinline__ void dma_rows32(const char* src, uint32_t stride, uint8_t* dst, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (2 * wave + i) + (lane >> 4);
+    const int cch = (lane & 15) ^ (r & 15);
+    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(r) * stride + (cch << 4),
+                                     (lds_void*)(dst + (2 * wave + i) * 1024), 16, 0, 0);
   }
 }
 
@@ -327,20 +364,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
 }
 
 // --------------------------------------------------------------------- dQ
-__global__ __launch_bounds__(256, 1) void bwd_dq_bf16(
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
     const bf16_t* __restrict__ kt, bf16_t* __restrict__ dq, TreeDev tr, int hq, int hkv, float c,
     float scale) {
   using M = Mfma<bf16_t>;
-  __shared__ __attribute__((aligned(1024))) uint8_t k_l0[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_l1[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_l0[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_l1[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t kt_l0[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t kt_l1[kBuf];
-  __shared__ __attribute__((aligned(16))) int32_t sp_l0[kHalf];
-  __shared__ __attribute__((aligned(16))) int32_t sp_l1[kHalf];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_l0[kQBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_l1[kQBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_l0[kQBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_l1[kQBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt_l0[kQBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt_l1[kQBuf];
+  __shared__ __attribute__((aligned(16))) int32_t sp_l0[kQStep];
+  __shared__ __attribute__((aligned(16))) int32_t sp_l1[kQStep];
 
   const int G = hq / hkv;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -372,9 +409,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16(
   int roff[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) roff[s] = lq * kRowB + (((2 * s + half) ^ (lq & 15)) << 4);
-  int toff[4];
+  int toff[2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) toff[s] = lq * kTRowB + (((2 * s + half) ^ ((lq >> 1) & 7)) << 4);
+  for (int s = 0; s < 2; ++s) toff[s] = lq * kQTRowB + (((2 * s + half) ^ ((lq >> 2) & 3)) << 4);
 
   f32x16_t dqacc[4];
 #pragma unroll
@@ -387,55 +424,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16(
   cint32* q_tile = cst(tr.q_tile);
   cint32* q_cls = cst(tr.q_cls);
   const int t_begin = q_ptr[qb];
-  const int n_steps = 2 * (q_ptr[qb + 1] - t_begin);
-  auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + (st >> 1)); };
+  const int n_steps = 4 * (q_ptr[qb + 1] - t_begin);  // four 32-key steps per tile
+  auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + (st >> 2)); };
   auto step_kb = [&](int st) { return q_tile[tile_of(st)] >> 1; };
 
-  int4 se4 = make_int4(0, 0, 0, 0);
+  int se1 = 0;
   auto issue_loads = [&](int st, uint8_t* kl, uint8_t* vl, uint8_t* ktl) {
     const int kbk = step_kb(st);
-    const int k0 = kbk * kTile + kHalf * (st & 1);
-    // the subtree ends first: their wait then leaves the DMA in flight
-    se4 = *reinterpret_cast<const int4*>(tr.se + k0 + 4 * (tid & 15));
-    dma_rows(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kl, wave, lane);
-    dma_rows(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vl, wave, lane);
-    const size_t toff0 = ((static_cast<size_t>(g) * tr.nb + kbk) * kTile * kTile + kHalf * (st & 1)) * 2;
-    dma_trows(reinterpret_cast<const char*>(kt) + toff0, ktl, wave, lane);
+    const int k0 = kbk * kTile + kQStep * (st & 3);
+    // the subtree end first: its wait then leaves the DMA in flight
+    se1 = tr.se[k0 + (tid & 31)];
+    dma_rows32(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kl, wave, lane);
+    dma_rows32(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vl, wave, lane);
+    const size_t toff0 = ((static_cast<size_t>(g) * tr.nb + kbk) * kTile * kTile + kQStep * (st & 3)) * 2;
+    dma_trows32(reinterpret_cast<const char*>(kt) + toff0, ktl, wave, lane);
   };
   auto store_span = [&](int st, int32_t* spl) {
-    if (tid < kHalf / 4) {
-      const int key = step_kb(st) * kTile + kHalf * (st & 1) + 4 * tid;
-      *reinterpret_cast<int4*>(spl + 4 * tid) =
-          make_int4(se4.x - key, se4.y - key - 1, se4.z - key - 2, se4.w - key - 3);
-    }
+    if (tid < kQStep) spl[tid] = se1 - (step_kb(st) * kTile + kQStep * (st & 3) + tid);
   };
 
   auto step = [&](int st, const uint8_t* kl, const uint8_t* vl, const uint8_t* ktl,
                   const int32_t* spl, uint8_t* nkl, uint8_t* nvl, uint8_t* nktl, int32_t* nspl) {
-    const int k0 = step_kb(st) * kTile + kHalf * (st & 1);
+    const int k0 = step_kb(st) * kTile + kQStep * (st & 3);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int st_next = st + 1 < n_steps ? st + 1 : st;
     issue_loads(st_next, nkl, nvl, nktl);
 
     const uint32_t bits = static_cast<uint32_t>(q_cls[tile_of(st)]);
-    const int A = qrow - k0 - 4 * half;
+    const int cls = (bits >> (2 * (4 * wave + (st & 3)))) & 3;
+    if (cls != 0) {
+      const int A = qrow - k0 - 4 * half;
+      // P^T (rows are keys, this lane's column is its query), dP^T = V.dO^T
+      f32x16_t p = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int cls = (bits >> (2 * (4 * wave + 2 * (st & 1) + kb2))) & 3;
-      if (cls == 0) continue;
-      // P^T: rows are keys, this lane's column is its query
-      f32x16_t p = f32x16_t{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) p = M::mma(lds_frag(kl, kb2 * 32 * kRowB + roff[s]), qf[s], p);
+      for (int s = 0; s < 8; ++s) {
+        p = M::mma(lds_frag(kl, roff[s]), qf[s], p);
+        dp = M::mma(lds_frag(vl, roff[s]), df[s], dp);
+      }
       if (cls == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int4 sp = *reinterpret_cast<const int4*>(spl + 32 * kb2 + 8 * i + 4 * half);
+          const int4 sp = *reinterpret_cast<const int4*>(spl + 8 * i + 4 * half);
           const int spv[4] = {sp.x, sp.y, sp.z, sp.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t dlt = static_cast<uint32_t>(A - (32 * kb2 + 8 * i + j));
+            const uint32_t dlt = static_cast<uint32_t>(A - (8 * i + j));
             const float e = fast_exp2(fmaf(p[4 * i + j], c, -lse2));
             p[4 * i + j] = dlt <= static_cast<uint32_t>(spv[j]) ? e : 0.f;
           }
@@ -444,19 +478,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16(
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(p[r], c, -lse2));
       }
-      // dP^T = V.dO^T, dS^T = P^T (dP^T - D)
-      f32x16_t dp = f32x16_t{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) dp = M::mma(lds_frag(vl, kb2 * 32 * kRowB + roff[s]), df[s], dp);
+      // dS^T = P^T (dP^T - D), dQ^T += K^T.dS^T
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r] *= dp[r] - dsum_q;
-      // dQ^T += K^T.dS^T
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const bf16x8_t sf = M::from_acc(p, s2);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          dqacc[b] = M::mma(lds_frag(ktl, b * 32 * kTRowB + toff[2 * kb2 + s2]), sf, dqacc[b]);
+          dqacc[b] = M::mma(lds_frag(ktl, b * 32 * kQTRowB + toff[s2]), sf, dqacc[b]);
       }
     }
     store_span(st_next, nspl);
@@ -466,7 +496,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16(
     issue_loads(0, k_l0, v_l0, kt_l0);
     store_span(0, sp_l0);
   }
-  for (int st = 0; st < n_steps; st += 2) {
+  for (int st = 0; st < n_steps; st += 2) {  // n_steps is a multiple of 4
     step(st, k_l0, v_l0, kt_l0, sp_l0, k_l1, v_l1, kt_l1, sp_l1);
     step(st + 1, k_l1, v_l1, kt_l1, sp_l1, k_l0, v_l0, kt_l0, sp_l0);
   }
