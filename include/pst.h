@@ -189,10 +189,8 @@ int pst_tree_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
                       int32_t dtype, float softmax_scale, void* stream);
 
 /* Bytes of device workspace pst_tree_attn_bwd needs for these shapes: the
- * float32 [hq, Np] per-row sums D = rowsum(dout * O), and for PST_BF16 with
- * head_dim 128 also transposed bf16 copies of q and dout ([hq][Np/128][128]
- * [128] each) and of k ([hkv][Np/128][128][128]).  The workspace is scratch:
- * its contents on entry do not matter and are overwritten.
+ * float32 [hq, Np] per-row sums D = rowsum(dout * O).  The workspace is
+ * scratch: its contents on entry do not matter and are overwritten.
  * Errors: PST_EINVAL (NULL), PST_ESHAPE, PST_EDTYPE. */
 int pst_tree_attn_bwd_workspace_bytes(const pst_tree_meta* meta, int32_t hq, int32_t hkv,
                                       int32_t head_dim, int32_t dtype, size_t* bytes);

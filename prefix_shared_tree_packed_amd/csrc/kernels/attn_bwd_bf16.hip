@@ -4,20 +4,19 @@
 // range of visible query blocks; dQ per query block over the forward tile
 // list), fed the way the forward kernel of attn_fwd_bf16.hip is fed:
 //
-//  * prep writes, next to D, transposed copies of Q and dO (per query head)
-//    and of K (per key/value head) into the caller's workspace: 128x128
-//    tiles, d-major, whose token positions are permuted inside each group of
-//    16 (token 16t+8a+4h+j sits at 16t+8h+4a+j).  A contraction over tokens
-//    then reads each MFMA operand as ONE 16-byte LDS load, and every tile --
-//    row-major or transposed -- reaches LDS by global_load_lds_dwordx4 (no
-//    VGPRs, no VALU) through two named buffers: 64 queries per step in the
-//    dK/dV kernel (one workgroup per CU, 129 KB), 32 keys per step in the dQ
-//    kernel (49 KB, two workgroups per CU, which measured 1.5x faster than
-//    one; the dK/dV kernel at 32 does not fit two waves per SIMD without
-//    spilling and measured slower).
-//  * Row-major LDS tiles store 16-byte chunk c of row r at c ^ (r & 15);
-//    transposed half-tiles (128-byte rows) store it at c ^ ((d >> 1) & 7),
-//    transposed 32-token slices (64-byte rows) at c ^ ((d >> 2) & 3).
+//  * Every tile reaches LDS row-major (token rows of 256 bytes) by
+//    global_load_lds_dwordx4 (no VGPRs, no VALU), double-buffered through
+//    two named buffers: Q and dO in 64-query steps for dK/dV (one workgroup
+//    per CU), K and V in 32-key steps for dQ (two workgroups per CU).
+//  * Products that contract over tokens need the tile transposed (dV^T +=
+//    dO^T.P, dK^T += Q^T.dS, dQ^T += K^T.dS^T).  Their A operands come from
+//    the same row-major tile through ds_read_b64_tr_b16: two transposing
+//    reads per MFMA operand, at nearly the rate of ordinary 16-byte reads,
+//    so no transposed copy exists anywhere and the prep pass only computes D.
+//  * 16-byte chunk c of tile row r sits at c ^ rsw(r), rsw(r) = 2 (r & 7) +
+//    ((r >> 3) & 1): 16 consecutive rows reading one chunk each hit 16
+//    distinct positions, and a transposing read (4 aligned rows x 2 adjacent
+//    chunks per 16 lanes) hits 8 distinct positions: no bank conflicts.
 //  * Work per (wave, 32x32 sub-block) is skipped when no pair is visible and
 //    masked element by element only when some are: (unsigned)(i - j) <=
 //    se[j] - j.
@@ -32,13 +31,12 @@ namespace pst {
 namespace {
 
 constexpr int D = 128;
-constexpr int kHalf = 64;           // tokens per pipeline step
-constexpr int kRowB = 256;          // row-major tile row: 128 bf16
-constexpr int kTRowB = 128;         // transposed half-tile row: 64 bf16
-constexpr int kBuf = kHalf * kRowB; // 16 KB per half-tile (either layout)
+constexpr int kRowB = 256;  // tile row: 128 bf16
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only: scalar loads
 
 __device__ __forceinline__ cint32* cst(const int32_t* p) { return (cint32*)(p); }
@@ -47,167 +45,97 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int byte_off) 
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + byte_off));
 }
 
-// token of the 128-block held at permuted position p
-__device__ __forceinline__ int perm_token(int p) {
-  return 16 * (p >> 4) + 8 * ((p >> 2) & 1) + 4 * ((p >> 3) & 1) + (p & 3);
-}
+__device__ __forceinline__ int rsw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
-// Row-major half-tile: 64 rows of 256 bytes starting at `src` (row stride
-// `stride` bytes) -> LDS, by the four waves with 4 DMA instructions each.
-__device__ __forceinline__ void dma_rows(const char* src, uint32_t stride, uint8_t* dst, int wave,
+// NROWS token rows of 256 bytes (row stride `stride` bytes in memory) ->
+// swizzled LDS tile; the four waves issue NROWS / 16 DMA instructions each,
+// instruction n covering rows 4n .. 4n+3.
+template <int NROWS>
+__device__ __forceinline__ void dma_tile(const char* src, uint32_t stride, uint8_t* dst, int wave,
                                          int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * (4 * wave + i) + (lane >> 4);
-    const int cch = (lane & 15) ^ (r & 15);
+  for (int i = 0; i < NROWS / 16; ++i) {
+    const int n = (NROWS / 16) * wave + i;
+    const int r = 4 * n + (lane >> 4);
+    const int cch = (lane & 15) ^ rsw(r);
     __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(r) * stride + (cch << 4),
-                                     (lds_void*)(dst + (4 * wave + i) * 1024), 16, 0, 0);
+                                     (lds_void*)(dst + n * 1024), 16, 0, 0);
   }
 }
 
-// Transposed half-tile: 128 rows (d) of 128 bytes (64 permuted positions)
-// starting at `src` (row stride 256 bytes in the workspace tile) -> LDS.
-__device__ __forceinline__ void dma_trows(const char* src, uint8_t* dst, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int d = 8 * (4 * wave + i) + (lane >> 3);
-    const int cch = (lane & 7) ^ ((d >> 1) & 7);
-    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(d) * kRowB + (cch << 4),
-                                     (lds_void*)(dst + (4 * wave + i) * 1024), 16, 0, 0);
-  }
+// Lane-constant parts of the transposing reads.  For rows d = D0 + lane % 32
+// (D0 a multiple of 32) and tokens T0 .. T0+15 (T0 a multiple of 16), MFMA
+// slot s of the lane holds token T0 + 8 (s / 4) + 4 half + s % 4 (the order in
+// which the score accumulators feed the B operand).  In each 16-lane group,
+// lane i addresses token T0 + 4 half + i / 4 (+8 for the second read) at
+// columns Dg + 4 (i % 4) .. +3 and receives column Dg + i of four tokens.
+struct TrOff {
+  int lo, hi;
+};
+__device__ __forceinline__ TrOff tr_offsets(int lane) {
+  const int g = lane >> 4, i = lane & 15, half = lane >> 5;
+  const int a = i & 3, j = i >> 2;
+  const int x = 2 * (g & 1) + (a >> 1);  // chunk of column Dg + 4a within the 32-column block
+  const int t0 = 4 * half + j, t1 = t0 + 8;
+  return {t0 * kRowB + (((x ^ rsw(t0)) << 4) | ((a & 1) << 3)),
+          t1 * kRowB + (((x ^ rsw(t1)) << 4) | ((a & 1) << 3))};
+}
+// A operand of X^T (X a row-major tile) for d-block D0 and token block T0.
+__device__ __forceinline__ bf16x8_t lds_tr_frag(const uint8_t* tile, TrOff o, int T0, int D0) {
+  const uint8_t* base = tile + T0 * kRowB;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + (o.lo ^ (2 * D0))));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + (o.hi ^ (2 * D0))));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, w);
 }
 
-// --------------------------------------------------------------------- prep
-// One workgroup per (128-block, head): items with x < hq transpose Q and dO
-// of query head x and compute D; items x >= hq transpose K of kv head x-hq.
-constexpr int kPrepStride = D + 2;  // LDS row stride (elements): column reads conflict-free
-
-__global__ __launch_bounds__(256) void bwd_prep_bf16(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ o,
-    const bf16_t* __restrict__ dout, float* __restrict__ dsum, bf16_t* __restrict__ qt,
-    bf16_t* __restrict__ dot, bf16_t* __restrict__ kt, int Np, int nb, int hq, int hkv) {
-  __shared__ __attribute__((aligned(16))) bf16_t ta[kTile * kPrepStride];
-  __shared__ __attribute__((aligned(16))) bf16_t tb[kTile * kPrepStride];
-  const int blk = blockIdx.x % nb;
-  const int x = blockIdx.x / nb;
-  const bool qitem = x < hq;
-  const int heads = qitem ? hq : hkv;
-  const int hx = qitem ? x : x - hq;
-  const int tid = threadIdx.x;
-  const size_t stride = static_cast<size_t>(heads) * D;
-  const bf16_t* a_src = (qitem ? q : k) + static_cast<size_t>(blk) * kTile * stride + hx * D;
-  const bf16_t* b_src = dout + static_cast<size_t>(blk) * kTile * stride + hx * D;
-
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int cidx = tid + 256 * i;
-    const int r = cidx >> 4, cc = cidx & 15;
-    const uint4 va = *reinterpret_cast<const uint4*>(a_src + r * stride + cc * 8);
-    uint32_t* da = reinterpret_cast<uint32_t*>(ta + r * kPrepStride + cc * 8);
-    da[0] = va.x; da[1] = va.y; da[2] = va.z; da[3] = va.w;
-    if (qitem) {
-      const uint4 vb = *reinterpret_cast<const uint4*>(b_src + r * stride + cc * 8);
-      uint32_t* db = reinterpret_cast<uint32_t*>(tb + r * kPrepStride + cc * 8);
-      db[0] = vb.x; db[1] = vb.y; db[2] = vb.z; db[3] = vb.w;
-    }
-  }
-  __syncthreads();
-
-  if (qitem) {
-    // D for the 128 rows: two threads per row, 64 dims each
-    const int r = tid >> 1, hh = tid & 1;
-    const bf16_t* orow = o + (static_cast<size_t>(blk) * kTile + r) * stride + hx * D + 64 * hh;
-    float acc = 0.f;
-#pragma unroll
-    for (int c8 = 0; c8 < 8; ++c8) {
-      const uint4 ov = *reinterpret_cast<const uint4*>(orow + 8 * c8);
-      const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
-      const uint32_t* dw = reinterpret_cast<const uint32_t*>(tb + r * kPrepStride + 64 * hh + 8 * c8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t dv = dw[e];
-        acc = fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(dv << 16), acc);
-        acc = fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(dv & 0xffff0000u), acc);
-      }
-    }
-    acc += __shfl_xor(acc, 1);
-    if (hh == 0) dsum[static_cast<size_t>(hx) * Np + blk * kTile + r] = acc;
-  }
-
-  // transposed tiles: chunk (d, c) holds positions 8c..8c+7 of row d
-  bf16_t* a_dst = (qitem ? qt : kt) + (static_cast<size_t>(hx) * nb + blk) * kTile * kTile;
-  bf16_t* b_dst = dot + (static_cast<size_t>(hx) * nb + blk) * kTile * kTile;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = tid + 256 * i;
-    const int c = idx >> 7, d = idx & 127;
-    uint32_t wa[4], wb[4];
+// --------------------------------------------------------------------- D
+// D[h][row] = dO[row][h] . O[row][h]: 16 lanes per (row, head), 16 bytes each.
+__global__ __launch_bounds__(256) void bwd_dsum_bf16(const bf16_t* __restrict__ o,
+                                                     const bf16_t* __restrict__ dout,
+                                                     float* __restrict__ dsum, int Np, int hq) {
+  const int pair = blockIdx.x * 16 + (threadIdx.x >> 4);  // row * hq + h
+  const int part = threadIdx.x & 15;
+  float acc = 0.f;
+  if (pair < Np * hq) {
+    const size_t off = static_cast<size_t>(pair) * D + part * 8;
+    const uint4 ov = *reinterpret_cast<const uint4*>(o + off);
+    const uint4 dov = *reinterpret_cast<const uint4*>(dout + off);
+    const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
+    const uint32_t dw[4] = {dov.x, dov.y, dov.z, dov.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r0 = perm_token(8 * c + 2 * e), r1 = perm_token(8 * c + 2 * e + 1);
-      wa[e] = static_cast<uint32_t>(ta[r0 * kPrepStride + d]) |
-              (static_cast<uint32_t>(ta[r1 * kPrepStride + d]) << 16);
-      if (qitem)
-        wb[e] = static_cast<uint32_t>(tb[r0 * kPrepStride + d]) |
-                (static_cast<uint32_t>(tb[r1 * kPrepStride + d]) << 16);
+      acc = fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(dw[e] << 16), acc);
+      acc = fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(dw[e] & 0xffff0000u), acc);
     }
-    *reinterpret_cast<uint4*>(a_dst + d * kTile + 8 * c) = make_uint4(wa[0], wa[1], wa[2], wa[3]);
-    if (qitem)
-      *reinterpret_cast<uint4*>(b_dst + d * kTile + 8 * c) = make_uint4(wb[0], wb[1], wb[2], wb[3]);
   }
-}
-
-// The dQ kernel streams 32 keys per pipeline step (8 KB per tile), so that
-// two workgroups share a CU and two waves share each SIMD.
-constexpr int kQStep = 32;
-constexpr int kQBuf = kQStep * kRowB;  // 8 KB
-constexpr int kQTRowB = kQStep * 2;    // transposed slice row: 64 bytes
-
-// Transposed slice: 128 rows (d) of 64 bytes (32 permuted positions) at `src`
-// (row stride 256 bytes in the workspace tile) -> LDS, chunk c of row d at
-// c ^ ((d >> 2) & 3); two DMA instructions per wave.
-__device__ __forceinline__ void dma_trows32(const char* src, uint8_t* dst, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int d = 16 * (2 * wave + i) + (lane >> 2);
-    const int cch = (lane & 3) ^ ((d >> 2) & 3);
-    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(d) * kRowB + (cch << 4),
-                                     (lds_void*)(dst + (2 * wave + i) * 1024), 16, 0, 0);
-  }
-}
-
-// Row-major slice: 32 rows of 256 bytes (row stride `stride`) -> LDS, chunk
-// c of row r at c ^ (r & 15); two DMA instructions per wave.
-__device__ __forceinline__ void dma_rows32(const char* src, uint32_t stride, uint8_t* dst, int wave,
-                                           int lane) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 4 * (2 * wave + i) + (lane >> 4);
-    const int cch = (lane & 15) ^ (r & 15);
-    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(r) * stride + (cch << 4),
-                                     (lds_void*)(dst + (2 * wave + i) * 1024), 16, 0, 0);
+  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (part == 0 && pair < Np * hq) {
+    const int row = pair / hq, h = pair - row * hq;
+    dsum[static_cast<size_t>(h) * Np + row] = acc;
   }
 }
 
 // --------------------------------------------------------------------- dK, dV
+constexpr int kKvStep = 64;                 // queries per step
+constexpr int kKvBuf = kKvStep * kRowB;     // 16 KB
+
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
-    const bf16_t* __restrict__ qt, const bf16_t* __restrict__ dot, bf16_t* __restrict__ dk,
-    bf16_t* __restrict__ dv, TreeDev tr, int hq, int hkv, float c, float scale) {
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, TreeDev tr, int hq, int hkv, float c,
+    float scale) {
   using M = Mfma<bf16_t>;
-  __shared__ __attribute__((aligned(1024))) uint8_t q_l0[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t q_l1[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t qt_l0[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t qt_l1[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t do_l0[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t do_l1[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t dt_l0[kBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t dt_l1[kBuf];
-  __shared__ __attribute__((aligned(16))) float ls_l0[kHalf];
-  __shared__ __attribute__((aligned(16))) float ls_l1[kHalf];
-  __shared__ __attribute__((aligned(16))) float dd_l0[kHalf];
-  __shared__ __attribute__((aligned(16))) float dd_l1[kHalf];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_l0[kKvBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_l1[kKvBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_l0[kKvBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_l1[kKvBuf];
+  __shared__ __attribute__((aligned(16))) float ls_l0[kKvStep];
+  __shared__ __attribute__((aligned(16))) float ls_l1[kKvStep];
+  __shared__ __attribute__((aligned(16))) float dd_l0[kKvStep];
+  __shared__ __attribute__((aligned(16))) float dd_l1[kKvStep];
 
   const int G = hq / hkv;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -234,12 +162,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
       vf[s] = M::load(v + off + 16 * s);
     }
   }
-  int roff[8];  // row-major operand chunk (row lq of a 32-row block, step s)
+  int roff[8];  // row operand: row lq of a 32-row block, contraction step s
 #pragma unroll
-  for (int s = 0; s < 8; ++s) roff[s] = lq * kRowB + (((2 * s + half) ^ (lq & 15)) << 4);
-  int toff[4];  // transposed operand chunk (row lq of a 32-row block, token step s)
-#pragma unroll
-  for (int s = 0; s < 4; ++s) toff[s] = lq * kTRowB + (((2 * s + half) ^ ((lq >> 1) & 7)) << 4);
+  for (int s = 0; s < 8; ++s) roff[s] = lq * kRowB + (((2 * s + half) ^ rsw(lq)) << 4);
+  const TrOff tro = tr_offsets(lane);
 
   f32x16_t dkacc[4], dvacc[4];
 #pragma unroll
@@ -257,18 +183,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
     const int r = rest % G;
     qb = kb + rest / G;
     h = g * G + r;
-    q0 = qb * kTile + kHalf * (st & 1);
+    q0 = qb * kTile + kKvStep * (st & 1);
   };
-  auto issue_loads = [&](int st, uint8_t* ql, uint8_t* qtl, uint8_t* dol, uint8_t* dtl, float* lsl,
-                         float* ddl) {
+  auto issue_loads = [&](int st, uint8_t* ql, uint8_t* dol, float* lsl, float* ddl) {
     int qb, h, q0;
     decode(st, qb, h, q0);
     const size_t row0 = static_cast<size_t>(q0) * q_bytes + static_cast<size_t>(h) * D * 2;
-    dma_rows(reinterpret_cast<const char*>(q) + row0, q_bytes, ql, wave, lane);
-    dma_rows(reinterpret_cast<const char*>(dout) + row0, q_bytes, dol, wave, lane);
-    const size_t toff0 = ((static_cast<size_t>(h) * tr.nb + qb) * kTile * kTile + kHalf * (st & 1)) * 2;
-    dma_trows(reinterpret_cast<const char*>(qt) + toff0, qtl, wave, lane);
-    dma_trows(reinterpret_cast<const char*>(dot) + toff0, dtl, wave, lane);
+    dma_tile<kKvStep>(reinterpret_cast<const char*>(q) + row0, q_bytes, ql, wave, lane);
+    dma_tile<kKvStep>(reinterpret_cast<const char*>(dout) + row0, q_bytes, dol, wave, lane);
     const size_t r0 = static_cast<size_t>(h) * tr.Np + q0;
     if (wave == 0)
       __builtin_amdgcn_global_load_lds(lse + r0 + lane, (lds_void*)lsl, 4, 0, 0);
@@ -276,15 +198,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
       __builtin_amdgcn_global_load_lds(dsum + r0 + lane, (lds_void*)ddl, 4, 0, 0);
   };
 
-  auto step = [&](int st, const uint8_t* ql, const uint8_t* qtl, const uint8_t* dol,
-                  const uint8_t* dtl, const float* lsl, const float* ddl, uint8_t* nql,
-                  uint8_t* nqtl, uint8_t* ndol, uint8_t* ndtl, float* nlsl, float* nddl) {
+  auto step = [&](int st, const uint8_t* ql, const uint8_t* dol, const float* lsl, const float* ddl,
+                  uint8_t* nql, uint8_t* ndol, float* nlsl, float* nddl) {
     int qb, h, q0;
     decode(st, qb, h, q0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // step st staged; step st-1 consumed
     const int st_next = st + 1 < n_steps ? st + 1 : st;
-    issue_loads(st_next, nql, nqtl, ndol, ndtl, nlsl, nddl);
+    issue_loads(st_next, nql, ndol, nlsl, nddl);
 
     const int A = q0 + 4 * half - key;  // (query - key) of register 0 of sub-block 0
 #pragma unroll
@@ -319,7 +240,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
         const bf16x8_t pf = M::from_acc(p, s2);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          dvacc[b] = M::mma(lds_frag(dtl, b * 32 * kTRowB + toff[2 * qs + s2]), pf, dvacc[b]);
+          dvacc[b] = M::mma(lds_tr_frag(dol, tro, 32 * qs + 16 * s2, 32 * b), pf, dvacc[b]);
       }
       // dP = dO.V^T, dS = P (dP - D)
       f32x16_t dp = f32x16_t{};
@@ -338,15 +259,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
         const bf16x8_t sf = M::from_acc(p, s2);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          dkacc[b] = M::mma(lds_frag(qtl, b * 32 * kTRowB + toff[2 * qs + s2]), sf, dkacc[b]);
+          dkacc[b] = M::mma(lds_tr_frag(ql, tro, 32 * qs + 16 * s2, 32 * b), sf, dkacc[b]);
       }
     }
   };
 
-  if (n_steps > 0) issue_loads(0, q_l0, qt_l0, do_l0, dt_l0, ls_l0, dd_l0);
+  if (n_steps > 0) issue_loads(0, q_l0, do_l0, ls_l0, dd_l0);
   for (int st = 0; st < n_steps; st += 2) {  // n_steps is even
-    step(st, q_l0, qt_l0, do_l0, dt_l0, ls_l0, dd_l0, q_l1, qt_l1, do_l1, dt_l1, ls_l1, dd_l1);
-    step(st + 1, q_l1, qt_l1, do_l1, dt_l1, ls_l1, dd_l1, q_l0, qt_l0, do_l0, dt_l0, ls_l0, dd_l0);
+    step(st, q_l0, do_l0, ls_l0, dd_l0, q_l1, do_l1, ls_l1, dd_l1);
+    step(st + 1, q_l1, do_l1, ls_l1, dd_l1, q_l0, do_l0, ls_l0, dd_l0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -364,18 +285,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
 }
 
 // --------------------------------------------------------------------- dQ
+// 32-key steps (two 8 KB tiles per stage, 33 KB of LDS): two workgroups per
+// CU, two waves per SIMD.
+constexpr int kQStep = 32;
+constexpr int kQBuf = kQStep * kRowB;  // 8 KB
+
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
-    const bf16_t* __restrict__ kt, bf16_t* __restrict__ dq, TreeDev tr, int hq, int hkv, float c,
-    float scale) {
+    bf16_t* __restrict__ dq, TreeDev tr, int hq, int hkv, float c, float scale) {
   using M = Mfma<bf16_t>;
   __shared__ __attribute__((aligned(1024))) uint8_t k_l0[kQBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t k_l1[kQBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t v_l0[kQBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t v_l1[kQBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t kt_l0[kQBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t kt_l1[kQBuf];
   __shared__ __attribute__((aligned(16))) int32_t sp_l0[kQStep];
   __shared__ __attribute__((aligned(16))) int32_t sp_l1[kQStep];
 
@@ -408,10 +331,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   const float dsum_q = dsum[static_cast<size_t>(h) * tr.Np + qrow];
   int roff[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) roff[s] = lq * kRowB + (((2 * s + half) ^ (lq & 15)) << 4);
-  int toff[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) toff[s] = lq * kQTRowB + (((2 * s + half) ^ ((lq >> 2) & 3)) << 4);
+  for (int s = 0; s < 8; ++s) roff[s] = lq * kRowB + (((2 * s + half) ^ rsw(lq)) << 4);
+  const TrOff tro = tr_offsets(lane);
 
   f32x16_t dqacc[4];
 #pragma unroll
@@ -429,27 +350,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   auto step_kb = [&](int st) { return q_tile[tile_of(st)] >> 1; };
 
   int se1 = 0;
-  auto issue_loads = [&](int st, uint8_t* kl, uint8_t* vl, uint8_t* ktl) {
-    const int kbk = step_kb(st);
-    const int k0 = kbk * kTile + kQStep * (st & 3);
+  auto issue_loads = [&](int st, uint8_t* kl, uint8_t* vl) {
+    const int k0 = step_kb(st) * kTile + kQStep * (st & 3);
     // the subtree end first: its wait then leaves the DMA in flight
     se1 = tr.se[k0 + (tid & 31)];
-    dma_rows32(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kl, wave, lane);
-    dma_rows32(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vl, wave, lane);
-    const size_t toff0 = ((static_cast<size_t>(g) * tr.nb + kbk) * kTile * kTile + kQStep * (st & 3)) * 2;
-    dma_trows32(reinterpret_cast<const char*>(kt) + toff0, ktl, wave, lane);
+    dma_tile<kQStep>(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kl, wave, lane);
+    dma_tile<kQStep>(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vl, wave, lane);
   };
   auto store_span = [&](int st, int32_t* spl) {
     if (tid < kQStep) spl[tid] = se1 - (step_kb(st) * kTile + kQStep * (st & 3) + tid);
   };
 
-  auto step = [&](int st, const uint8_t* kl, const uint8_t* vl, const uint8_t* ktl,
-                  const int32_t* spl, uint8_t* nkl, uint8_t* nvl, uint8_t* nktl, int32_t* nspl) {
+  auto step = [&](int st, const uint8_t* kl, const uint8_t* vl, const int32_t* spl, uint8_t* nkl,
+                  uint8_t* nvl, int32_t* nspl) {
     const int k0 = step_kb(st) * kTile + kQStep * (st & 3);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int st_next = st + 1 < n_steps ? st + 1 : st;
-    issue_loads(st_next, nkl, nvl, nktl);
+    issue_loads(st_next, nkl, nvl);
 
     const uint32_t bits = static_cast<uint32_t>(q_cls[tile_of(st)]);
     const int cls = (bits >> (2 * (4 * wave + (st & 3)))) & 3;
@@ -486,19 +404,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
         const bf16x8_t sf = M::from_acc(p, s2);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          dqacc[b] = M::mma(lds_frag(ktl, b * 32 * kQTRowB + toff[s2]), sf, dqacc[b]);
+          dqacc[b] = M::mma(lds_tr_frag(kl, tro, 16 * s2, 32 * b), sf, dqacc[b]);
       }
     }
     store_span(st_next, nspl);
   };
 
   if (n_steps > 0) {
-    issue_loads(0, k_l0, v_l0, kt_l0);
+    issue_loads(0, k_l0, v_l0);
     store_span(0, sp_l0);
   }
   for (int st = 0; st < n_steps; st += 2) {  // n_steps is a multiple of 4
-    step(st, k_l0, v_l0, kt_l0, sp_l0, k_l1, v_l1, kt_l1, sp_l1);
-    step(st + 1, k_l1, v_l1, kt_l1, sp_l1, k_l0, v_l0, kt_l0, sp_l0);
+    step(st, k_l0, v_l0, sp_l0, k_l1, v_l1, sp_l1);
+    step(st + 1, k_l1, v_l1, sp_l1, k_l0, v_l0, sp_l0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -516,8 +434,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
 }  // namespace
 
 size_t attn_bwd_bf16_d128_workspace(int Np, int hq, int hkv) {
-  return static_cast<size_t>(Np) * hq * sizeof(float) +
-         (2 * static_cast<size_t>(hq) + hkv) * Np * D * sizeof(bf16_t);
+  (void)hkv;
+  return static_cast<size_t>(Np) * hq * sizeof(float);
 }
 
 hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v, const void* o,
@@ -525,26 +443,21 @@ hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v
                                      void* ws, const TreeDev& tr, int hq, int hkv, float scale,
                                      hipStream_t stream) {
   const float c = scale * kLog2e;
-  const size_t Np = tr.Np;
   float* dsum = static_cast<float*>(ws);
-  bf16_t* qt = reinterpret_cast<bf16_t*>(dsum + Np * hq);
-  bf16_t* dot = qt + Np * hq * D;
-  bf16_t* kt = dot + Np * hq * D;
-  hipLaunchKernelGGL(bwd_prep_bf16, dim3(static_cast<unsigned>(tr.nb) * (hq + hkv)), dim3(256), 0,
-                     stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), dsum, qt, dot, kt,
-                     tr.Np, tr.nb, hq, hkv);
+  const unsigned pairs = static_cast<unsigned>(tr.Np) * hq;
+  hipLaunchKernelGGL(bwd_dsum_bf16, dim3((pairs + 15) / 16), dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), dsum, tr.Np, hq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dkdv_bf16, dim3(static_cast<unsigned>(tr.nb) * hkv), dim3(256), 0, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum, qt, dot,
+                     static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum,
                      static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), tr, hq, hkv, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_bf16, dim3(static_cast<unsigned>(tr.nb) * hq), dim3(256), 0, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum, kt,
+                     static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum,
                      static_cast<bf16_t*>(dq), tr, hq, hkv, c, scale);
   return hipGetLastError();
 }

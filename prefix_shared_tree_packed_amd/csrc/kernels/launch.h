@@ -25,9 +25,7 @@ hipError_t launch_attn_fwd_bf16_d128(const void* q, const void* k, const void* v
                                      float* lse, const TreeDev& tr, int hq, int hkv, float scale,
                                      hipStream_t stream);
 
-// workspace: float32 [hq, Np] (the per-row dO.O sums); for bf16 / head_dim
-// 128 followed by the transposed tiles of attn_bwd_bf16.hip, in all
-// attn_bwd_bf16_d128_workspace bytes.
+// workspace: float32 [hq, Np] (the per-row dO.O sums).
 hipError_t launch_attn_bwd(int dtype, int head_dim, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout, void* dq, void* dk,
                            void* dv, void* workspace, const TreeDev& tr, int hq, int hkv,
