@@ -6,15 +6,13 @@
 //
 //  * Each non-empty 128x128 tile is walked as two 64-key halves through a
 //    double-buffered LDS pipeline: while the waves compute one half, the next
-//    half's K rows stream global -> LDS directly (global_load_lds_dwordx4: no
-//    VGPRs, no VALU) and its V rows are already in registers.  One barrier per
-//    half; two 32 KB buffers keep two workgroups per CU.
-//  * K rows are 256 bytes with the 16-byte chunk c of row r stored at c ^ (r & 15).
-//  * V is transposed in registers (4 keys x 8 dims per thread, v_perm_b32)
-//    into d-major rows whose keys are permuted inside each group of 16 (key
-//    16t+8a+4h+j sits at 16t+8h+4a+j), so every MFMA operand of V^T is ONE
-//    16-byte LDS read; the 16-byte chunk c of row d sits at c ^ ((d >> 1) & 7),
-//    which keeps those reads bank-conflict free.
+//    half's K and V rows stream global -> LDS directly (global_load_lds_dwordx4:
+//    no VGPRs, no VALU) into row-major tiles (swizzle of lds_tiles.h).  One
+//    barrier per half; 66 KB of LDS keep two workgroups per CU.
+//  * K rows are the A operand of S^T = K.Q^T as they stand (one 16-byte read
+//    per MFMA operand); the V^T operands of O^T += V^T.P^T come from the same
+//    row-major V tile through two ds_read_b64_tr_b16 transposing reads, whose
+//    slot order is the order in which the score accumulators feed P^T.
 //  * The mask is evaluated per (wave, 32-key block): a block whose keys no
 //    query of the wave sees is skipped (no MFMA, no exp), a block every query
 //    sees runs unmasked, and only the rest pay the per-element test
@@ -24,6 +22,7 @@
 //    rescaled only when a row's max grows by more than 2^8, so exponentials
 //    stay below 256 and most steps skip the rescale.
 #include "launch.h"
+#include "lds_tiles.h"
 #include "mfma.h"
 
 #include <cmath>
@@ -34,18 +33,12 @@ namespace {
 constexpr int D = 128;
 constexpr int kHalf = 64;                 // keys per pipeline step
 constexpr int kKRow = D * 2;              // K row: 256 B
-constexpr int kVRow = kHalf * 2;          // V^T row: 128 B (64 keys)
-constexpr int kBufBytes = kHalf * kKRow;  // 16 KB for K, 16 KB for V^T
+constexpr int kBufBytes = kHalf * kKRow;  // 16 KB for K, 16 KB for V
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only: scalar loads
 
 __device__ __forceinline__ cint32* cst(const int32_t* p) { return (cint32*)(p); }
-
-__device__ __forceinline__ uint32_t word(const uint4& u, int p) {
-  return p == 0 ? u.x : p == 1 ? u.y : p == 2 ? u.z : u.w;
-}
 
 __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int byte_off) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + byte_off));
@@ -89,31 +82,17 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = M::load(qp + 16 * s);
   }
-  // LDS byte offsets of this lane's 16-byte operand chunks: K rows for
-  // contraction step s, V^T rows for 16-key step s
+  // LDS byte offsets of this lane's 16-byte K chunk for contraction step s
+  // (row lq of a 32-key block); V^T operands come through transposing reads
   int koff_rd[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) koff_rd[s] = lq * kKRow + (((2 * s + half) ^ (lq & 15)) << 4);
-  int voff_rd[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) voff_rd[s] = lq * kVRow + (((2 * s + half) ^ ((lq >> 1) & 7)) << 4);
+  for (int s = 0; s < 8; ++s) koff_rd[s] = lq * kKRow + (((2 * s + half) ^ rsw(lq)) << 4);
+  const TrOff tro = tr_offsets(lane);
 
   // Global loads: a wave-uniform base pointer plus a 32-bit lane offset.
   const uint32_t kv_bytes = static_cast<uint32_t>(hkv) * D * 2;  // one token's K (or V) rows
   const char* kgb = reinterpret_cast<const char*>(k + static_cast<size_t>(g) * D);
   const char* vgb = reinterpret_cast<const char*>(v + static_cast<size_t>(g) * D);
-  // K: wave instruction i writes rows 4(4*wave+i) .. +3 of the half, lane ->
-  // row +lane/16, stored chunk lane%16 holding logical chunk (lane%16)^(row&15)
-  uint32_t koff_ld[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    koff_ld[i] = (lane >> 4) * kv_bytes + (((lane & 15) ^ ((4 * i + (lane >> 4)) & 15)) << 4);
-  // V: this thread stages keys 4*kq .. 4*kq+3 of the half, dims 8*vcc .. +7
-  const int kq = lane & 15;
-  const int vcc = tid >> 4;
-  const uint32_t voff_ld = 4 * kq * kv_bytes + vcc * 16;
-  // stored key position of the quad: key 16t+8a+4h (+j) -> 16t+8h+4a (+j)
-  const int vpos = 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
 
   f32x16_t oacc[4];
 #pragma unroll
@@ -129,34 +108,17 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
   auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + (st >> 1)); };
   auto step_key0 = [&](int st) { return (q_tile[tile_of(st)] >> 1) * kTile + kHalf * (st & 1); };
 
-  uint4 vreg[4];
   int4 se4 = make_int4(0, 0, 0, 0);
-  auto issue_loads = [&](int st, uint8_t* kdst) {
+  auto issue_loads = [&](int st, uint8_t* kdst, uint8_t* vdst) {
     const int k0 = step_key0(st);
-    const char* kt = kgb + static_cast<size_t>(k0) * kv_bytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(kt + static_cast<size_t>(4 * (4 * wave + i)) * kv_bytes + koff_ld[i],
-                                       (lds_void*)(kdst + (4 * wave + i) * 1024), 16, 0, 0);
-    const char* vt = vgb + static_cast<size_t>(k0) * kv_bytes;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      vreg[j] = *reinterpret_cast<const uint4*>(vt + static_cast<size_t>(j) * kv_bytes + voff_ld);
     // every lane loads (lanes past 16 repeat a quad; only 16 are stored), so
-    // no load sits in a divergent branch
+    // no load sits in a divergent branch; first, so that its wait leaves the
+    // DMA in flight
     se4 = *reinterpret_cast<const int4*>(tr.se + k0 + 4 * (tid & 15));
+    dma_tile<kHalf>(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kdst, wave, lane);
+    dma_tile<kHalf>(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vdst, wave, lane);
   };
-  auto store_v = [&](int st, uint8_t* vdst, int32_t* sdst) {
-#pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
-      uint2 outv;
-      outv.x = __builtin_amdgcn_perm(word(vreg[1], mm >> 1), word(vreg[0], mm >> 1), sel);
-      outv.y = __builtin_amdgcn_perm(word(vreg[3], mm >> 1), word(vreg[2], mm >> 1), sel);
-      const int d = 8 * vcc + mm;
-      const int chunk = (vpos >> 3) ^ ((d >> 1) & 7);
-      *reinterpret_cast<uint2*>(vdst + d * kVRow + (chunk << 4) + (vpos & 7) * 2) = outv;
-    }
+  auto store_span = [&](int st, int32_t* sdst) {
     if (tid < kHalf / 4) {
       const int key = step_key0(st) + 4 * tid;
       const int4 span = make_int4(se4.x - key, se4.y - key - 1, se4.z - key - 2, se4.w - key - 3);
@@ -173,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
     // into the idle buffer (in bounds, never read) so the code stays
     // branch-free and the compiler keeps the DMA and the reads apart
     const int st_next = st + 1 < n_steps ? st + 1 : st;
-    issue_loads(st_next, knext);
+    issue_loads(st_next, knext, vnext);
 
     // class of this wave's two 32x32 sub-blocks: 0 empty, 1 partial, 2 full
     const uint32_t bits = static_cast<uint32_t>(q_cls[tile_of(st)]);
@@ -252,18 +214,18 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
             const bf16x8_t pf = M::from_acc(sacc[kb], s2);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-              oacc[b] = M::mma(lds_frag(vcur, b * 32 * kVRow + voff_rd[2 * kb + s2]), pf, oacc[b]);
+              oacc[b] = M::mma(lds_tr_frag(vcur, tro, 32 * kb + 16 * s2, 32 * b), pf, oacc[b]);
           }
         }
       }
     }
 
-    store_v(st_next, vnext, snext);
+    store_span(st_next, snext);
   };
 
   if (n_steps > 0) {
-    issue_loads(0, k_lds0);
-    store_v(0, vt_lds0, span_lds0);
+    issue_loads(0, k_lds0, vt_lds0);
+    store_span(0, span_lds0);
   }
   for (int st = 0; st < n_steps; st += 2) {  // n_steps is even: two halves per tile
     step(st, k_lds0, vt_lds0, span_lds0, k_lds1, vt_lds1, span_lds1);
