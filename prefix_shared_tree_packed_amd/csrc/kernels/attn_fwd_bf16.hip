@@ -4,11 +4,14 @@
 // S^T = K.Q^T with the query in the lane, O^T += V^T.P^T fed from the score
 // accumulators); what changes is how every step is fed:
 //
-//  * Each non-empty 128x128 tile is walked as two 64-key halves through a
-//    double-buffered LDS pipeline: while the waves compute one half, the next
-//    half's K and V rows stream global -> LDS directly (global_load_lds_dwordx4:
+//  * Each non-empty 128x128 tile is walked in four 32-key steps through a
+//    double-buffered LDS pipeline: while the waves compute one step, the next
+//    step's K and V rows stream global -> LDS directly (global_load_lds_dwordx4:
 //    no VGPRs, no VALU) into row-major tiles (swizzle of lds_tiles.h).  One
-//    barrier per half; 66 KB of LDS keep two workgroups per CU.
+//    barrier per step.  33 KB of LDS and 168 VGPRs let three workgroups share
+//    a CU (three waves per SIMD), which measured faster than 64-key steps at
+//    two workgroups per CU: the kernel is bound by latency, not by LDS or
+//    HBM bandwidth.
 //  * K rows are the A operand of S^T = K.Q^T as they stand (one 16-byte read
 //    per MFMA operand); the V^T operands of O^T += V^T.P^T come from the same
 //    row-major V tile through two ds_read_b64_tr_b16 transposing reads, whose
@@ -31,9 +34,11 @@ namespace pst {
 namespace {
 
 constexpr int D = 128;
-constexpr int kHalf = 64;                 // keys per pipeline step
+constexpr int kStep = 32;              // keys per pipeline step
+constexpr int kSpt = kTile / kStep;    // steps per tile
+constexpr int kNkb = kStep / 32;       // 32-key blocks per step
 constexpr int kKRow = D * 2;              // K row: 256 B
-constexpr int kBufBytes = kHalf * kKRow;  // 16 KB for K, 16 KB for V
+constexpr int kBufBytes = kStep * kKRow;  // 8 KB for K, 8 KB for V
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
 
 typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only: scalar loads
@@ -44,7 +49,7 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int byte_off) 
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + byte_off));
 }
 
-__global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
+__global__ __launch_bounds__(256, 3) void tree_attn_fwd_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ o, float* __restrict__ lse, TreeDev tr, int hq, int hkv, float c) {
   using M = Mfma<bf16_t>;
@@ -55,8 +60,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t vt_lds0[kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t vt_lds1[kBufBytes];
-  __shared__ __attribute__((aligned(16))) int32_t span_lds0[kHalf];
-  __shared__ __attribute__((aligned(16))) int32_t span_lds1[kHalf];
+  __shared__ __attribute__((aligned(16))) int32_t span_lds0[kStep];
+  __shared__ __attribute__((aligned(16))) int32_t span_lds1[kStep];
 
   const int G = hq / hkv;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -103,10 +108,10 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
   cint32* q_tile = cst(tr.q_tile);
   cint32* q_cls = cst(tr.q_cls);
   const int t_begin = q_ptr[qb];
-  const int n_steps = 2 * (q_ptr[qb + 1] - t_begin);
+  const int n_steps = kSpt * (q_ptr[qb + 1] - t_begin);
   // tile index of a step, pinned to an SGPR so metadata reads stay scalar
-  auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + (st >> 1)); };
-  auto step_key0 = [&](int st) { return (q_tile[tile_of(st)] >> 1) * kTile + kHalf * (st & 1); };
+  auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + st / kSpt); };
+  auto step_key0 = [&](int st) { return (q_tile[tile_of(st)] >> 1) * kTile + kStep * (st % kSpt); };
 
   int4 se4 = make_int4(0, 0, 0, 0);
   auto issue_loads = [&](int st, uint8_t* kdst, uint8_t* vdst) {
@@ -115,11 +120,11 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
     // no load sits in a divergent branch; first, so that its wait leaves the
     // DMA in flight
     se4 = *reinterpret_cast<const int4*>(tr.se + k0 + 4 * (tid & 15));
-    dma_tile<kHalf>(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kdst, wave, lane);
-    dma_tile<kHalf>(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vdst, wave, lane);
+    dma_tile<kStep>(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kdst, wave, lane);
+    dma_tile<kStep>(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vdst, wave, lane);
   };
   auto store_span = [&](int st, int32_t* sdst) {
-    if (tid < kHalf / 4) {
+    if (tid < kStep / 4) {
       const int key = step_key0(st) + 4 * tid;
       const int4 span = make_int4(se4.x - key, se4.y - key - 1, se4.z - key - 2, se4.w - key - 3);
       *reinterpret_cast<int4*>(sdst + 4 * tid) = span;
@@ -139,15 +144,18 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
 
     // class of this wave's two 32x32 sub-blocks: 0 empty, 1 partial, 2 full
     const uint32_t bits = static_cast<uint32_t>(q_cls[tile_of(st)]);
-    int cls[2];
+    int cls[kNkb];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) cls[kb] = (bits >> (2 * (4 * wave + 2 * (st & 1) + kb))) & 3;
+    for (int kb = 0; kb < kNkb; ++kb) cls[kb] = (bits >> (2 * (4 * wave + kNkb * (st % kSpt) + kb))) & 3;
 
-    if (cls[0] | cls[1]) {
-      // S^T = K.Q^T for the non-empty 32-key blocks
-      f32x16_t sacc[2];
+    bool any_cls = false;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kNkb; ++kb) any_cls |= cls[kb] != 0;
+    if (any_cls) {
+      // S^T = K.Q^T for the non-empty 32-key blocks
+      f32x16_t sacc[kNkb];
+#pragma unroll
+      for (int kb = 0; kb < kNkb; ++kb) {
         sacc[kb] = f32x16_t{};
         if (cls[kb]) {
 #pragma unroll
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
       float mx = -INFINITY;
       const int A = qrow - k0 - 4 * half;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kNkb; ++kb) {
         if (cls[kb] == 1) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
       const float negm = m_used == -INFINITY ? 0.f : -m_used;
       float sum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kNkb; ++kb) {
         if (cls[kb]) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
 
       // O^T += V^T.P^T
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kNkb; ++kb) {
         if (cls[kb]) {
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_fwd_bf16_d128(
     issue_loads(0, k_lds0, vt_lds0);
     store_span(0, span_lds0);
   }
-  for (int st = 0; st < n_steps; st += 2) {  // n_steps is even: two halves per tile
+  for (int st = 0; st < n_steps; st += 2) {  // n_steps is a multiple of kSpt, so even
     step(st, k_lds0, vt_lds0, span_lds0, k_lds1, vt_lds1, span_lds1);
     step(st + 1, k_lds1, vt_lds1, span_lds1, k_lds0, vt_lds0, span_lds0);
   }
