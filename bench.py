@@ -46,7 +46,8 @@ def kernel_sources(kernel, dtype, head_dim):
     files = {"attn_fwd": ["attn_fwd_bf16.hip" if fast else "attn_fwd.hip"],
              "attn_bwd": ["attn_bwd_bf16.hip" if fast else "attn_bwd.hip"],
              "gather": ["gather.hip"]}[kernel]
-    return [os.path.join(KDIR, f) for f in files + ["common.h", "mfma.h"]]
+    shared = ["common.h", "mfma.h"] + (["lds_tiles.h"] if fast and kernel != "gather" else [])
+    return [os.path.join(KDIR, f) for f in files + shared]
 
 
 def sources_sha256(paths):
