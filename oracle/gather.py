@@ -30,7 +30,9 @@ def row_lse_entropy(rows: np.ndarray):
     z = e.sum(axis=1, keepdims=True)
     lse = (m + np.log(z))[:, 0]
     p = e / z
-    ent = lse - (p * x).sum(axis=1)
+    # a zero-probability entry adds nothing to -sum p log p (0 log 0 = 0),
+    # also where its logit is -inf
+    ent = lse - (p * np.where(p > 0, x, 0.0)).sum(axis=1)
     return lse, ent
 
 

@@ -11,8 +11,9 @@
 // different next tokens.  The host's row_out_ptr / out_pos / out_tgt map
 // lists those outputs per row.
 //
-// One 256-thread workgroup per row; pad rows (no outputs) return at once.  Each thread streams 16-byte chunks
-// (four in flight) and keeps an online (max, sum e^(x-max), sum e^(x-max)*x)
+// One 256-thread workgroup per row; pad rows (no outputs) return at once.
+// Each thread streams 16-byte chunks (eight in flight, the last batch
+// masked) and keeps an online (max, sum e^(x-max), sum e^(x-max)*x)
 // triple; triples merge across the wave with butterfly shuffles and across
 // the four waves through LDS.  Pad rows are never read.  The kernel is
 // HBM-bound: N*V*sizeof(logit) bytes in, 8 bytes per output out.
@@ -51,12 +52,15 @@ __device__ __forceinline__ void absorb(Acc& a, const float (&x)[N]) {
     a.t *= f;
     a.m = cm;
   }
+  if (a.m == -INFINITY) return;  // nothing but -inf so far
   const float mb = a.m * kLog2e;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const float e = fast_exp2(fmaf(x[i], kLog2e, -mb));
     a.s += e;
-    a.t = fmaf(e, x[i], a.t);
+    // p log-term of a zero probability is 0 (also for x = -inf, where e * x
+    // would be NaN)
+    a.t = fmaf(e, e > 0.f ? x[i] : 0.f, a.t);
   }
 }
 
@@ -113,12 +117,18 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const u32x4_t* body = reinterpret_cast<const u32x4_t*>(x + head);
 
+  // every batch keeps kUnroll loads in flight per thread; chunks past the
+  // end read as -inf (no contribution)
+  const uint32_t ninf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
+  const u32x4_t pad = {ninf, ninf, ninf, ninf};
   Acc a{-INFINITY, 0.f, 0.f};
-  int64_t ch = tid;
-  for (; ch + (kUnroll - 1) * kThreads < nch; ch += kUnroll * kThreads) {
+  for (int64_t base = 0; base < nch; base += kUnroll * kThreads) {
     u32x4_t u[kUnroll];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) u[j] = __builtin_nontemporal_load(body + ch + j * kThreads);
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = base + tid + j * kThreads;
+      u[j] = c < nch ? __builtin_nontemporal_load(body + c) : pad;
+    }
     // one max and one rescale per batch, then the exponentials
     float f[kUnroll * EPC];
 #pragma unroll
@@ -128,12 +138,6 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
 #pragma unroll
       for (int e = 0; e < EPC; ++e) f[j * EPC + e] = g[e];
     }
-    absorb(a, f);
-  }
-  for (; ch < nch; ch += kThreads) {
-    float f[EPC];
-    const u32x4_t w = body[ch];
-    unpack<T>(uint4{w.x, w.y, w.z, w.w}, f);
     absorb(a, f);
   }
   for (int64_t e = tid; e < head; e += kThreads) {

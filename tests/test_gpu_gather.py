@@ -127,3 +127,27 @@ def test_gather_forest_meta_matches_per_tree(gpu_lib):
         fmeta.destroy()
     finally:
         case.close()
+
+
+def test_gather_masked_vocabulary(gpu_lib):
+    """Rows whose vocabulary is partly masked to -inf (odd vocabulary, so
+    rows are unaligned and also take the element-wise head/tail path):
+    finite entropy and logprobs equal to the oracle's, where 0 log 0 = 0."""
+    import torch
+    rng = np.random.default_rng(17)
+    seqs = prompt_groups(rng, 2, 40, 3, 10, 60, vocab=300)
+    case = Case(seqs, 256)
+    try:
+        for dtype in ("bf16", "f32"):
+            for t, tree in enumerate(case.ref.trees):
+                logits = make_tensor((tree.n_padded, 1003), dtype, 1000 + t, "cuda", std=2.0)
+                logits[:, 300:] = float("-inf")   # every target (< 300) stays visible
+                lp, ent = gpu_lib.gather_tree_logprobs_entropy(logits, case.metas[t])
+                lph, enth = host(lp), host(ent)
+                assert np.isfinite(enth).all() and np.isfinite(lph).all()
+                lg = host(logits[:tree.n_tokens])
+                rlp, rent = oracle.gather_logprobs_entropy(tree, seqs, lg)
+                assert_close(lph, rlp, dtype, "logprob[masked]", **_tol(dtype))
+                assert_close(enth, rent, dtype, "entropy[masked]", **_tol(dtype))
+    finally:
+        case.close()

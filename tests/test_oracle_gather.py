@@ -5,12 +5,15 @@
    through the index maps;
  * closed forms: uniform logits give logprob -log V and entropy log V; a
    dominant spike on the next token gives logprob -> 0 and entropy -> 0;
+   k equal logits with the rest of the vocabulary at -inf (a masked
+   vocabulary) give logprob -log k and entropy log k;
  * the worked example yields 11 outputs in sequence order, last of each 0.
 """
 
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -91,3 +94,20 @@ def test_gather_worked_example_layout():
         assert lp[p] == (0.0 if e is None else logits[e[0], e[1]] - lse[e[0]])
     rows = [0, 1, 2, 3, 0, 1, 4, 5, 0, 6, 7]
     np.testing.assert_allclose(ent, H[rows], atol=0)
+
+
+def test_gather_masked_vocabulary_closed_form():
+    """Entries at -inf have probability 0 and add nothing to the entropy."""
+    V, k = 12, 5
+    row = np.full((1, V), -np.inf)
+    row[0, 3:3 + k] = 0.7
+    lse, ent = oracle.row_lse_entropy(row)
+    assert lse[0] == pytest.approx(0.7 + math.log(k), abs=1e-12)
+    assert ent[0] == pytest.approx(math.log(k), abs=1e-12)
+    seqs = [np.array([1, 4, 6], dtype=np.int32)]
+    f = oracle.build_forest(seqs, 128)
+    logits = np.full((128, V), -np.inf)
+    logits[:, 3:3 + k] = 0.7
+    lp, h = oracle.gather_logprobs_entropy(f.trees[0], seqs, logits)
+    assert np.allclose(lp, [-math.log(k), -math.log(k), 0.0], atol=1e-12)
+    assert np.allclose(h, math.log(k), atol=1e-12)
