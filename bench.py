@@ -303,6 +303,18 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, sizes, fb, target_s):
     """The oracle, as it stands, on a bounded sample of the same workload:
     the dense-mask float64 forward of tree 0 for as many query heads of the
@@ -344,6 +356,7 @@ def cpu_baseline(w, sizes, fb, target_s):
         "sample": f"dense-mask float64 forward of tree 0 ({tree.n_tokens} tokens), "
                   f"{heads} of {w.hq} query heads, {elapsed:.1f} s",
         "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model(),
     }
     if w.gather:
         sids = tree.seq_ids[:2]

@@ -12,7 +12,8 @@ Modules:
   tree        sequence intake, first-fit-decreasing trie packing, chain
               compression, preorder flattening, padding, tile classes
   attention   dense ancestor mask, masked-softmax attention forward/backward
-  gather      per-sequence next-token log-probabilities and entropies
+  gather      per-sequence next-token log-probabilities and entropies, and
+              their gradient with respect to the packed logits
   accounting  tree_token_ratio, visible pairs, FLOP counts
 """
 
@@ -23,5 +24,7 @@ from .tree import (  # noqa: F401
 from .attention import (  # noqa: F401
     ancestors, dense_mask, attn_fwd, attn_bwd, attn_fwd_rows, attn_bwd_rows,
 )
-from .gather import gather_logprobs_entropy, row_lse_entropy  # noqa: F401
+from .gather import (  # noqa: F401
+    gather_logprobs_entropy, gather_logprobs_entropy_bwd, row_lse_entropy,
+)
 from .accounting import forest_stats  # noqa: F401

@@ -13,6 +13,16 @@ logits row of the tree token holding s[t] and take
 in float64, natural logs, temperature 1.  Outputs of the sequences of one tree
 are concatenated in ascending input index (the page's last step concatenates
 per-sequence results).
+
+The backward (the loss path the same section implies: training differentiates
+these log-probabilities and entropies) is the plain chain rule, output by
+output: with log p = x - lse and H = lse - sum p x,
+
+    d logprob[t] / d x_v = [v = s[t+1]] - p_v          (t < L-1; 0 at t = L-1)
+    d entropy[t] / d x_v = -p_v (log p_v + H)
+
+summed over every (sequence, position) whose token's row is x; rows that no
+output reads (pad rows) get zero.
 """
 
 from __future__ import annotations
@@ -52,3 +62,34 @@ def gather_logprobs_entropy(tree: Tree, seqs, logits):
         outs_lp.append(lp)
         outs_h.append(ent)
     return np.concatenate(outs_lp), np.concatenate(outs_h)
+
+
+def gather_logprobs_entropy_bwd(tree: Tree, seqs, logits, dlogprobs, dentropy):
+    """Gradient of sum(dlogprobs * logprobs + dentropy * entropy) with respect
+    to the logits [Np, V] of one tree, where logprobs/entropy are
+    gather_logprobs_entropy(tree, seqs, logits).  Returns float64 [Np, V]."""
+    x_all = np.asarray(logits, dtype=np.float64)
+    grad = np.zeros_like(x_all)
+    dlp = np.asarray(dlogprobs, dtype=np.float64)
+    dh = np.asarray(dentropy, dtype=np.float64)
+    off = 0
+    for sid in tree.seq_ids:
+        seq = np.asarray(seqs[sid])
+        idx = tree.seq_index[sid]
+        for t in range(len(seq)):
+            row = int(idx[t])
+            x = x_all[row]
+            m = x.max()
+            e = np.exp(x - m)
+            z = e.sum()
+            p = e / z
+            logp = x - (m + np.log(z))
+            ent = -(p * np.where(p > 0, logp, 0.0)).sum()
+            # entropy term; a zero-probability entry has zero derivative
+            grad[row] += dh[off + t] * (-p * np.where(p > 0, logp + ent, 0.0))
+            if t < len(seq) - 1:
+                g = -p.copy()
+                g[int(seq[t + 1])] += 1.0
+                grad[row] += dlp[off + t] * g
+        off += len(seq)
+    return grad
