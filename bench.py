@@ -88,6 +88,10 @@ def parse():
     ap.add_argument("--workload", default="grpo",
                     help="tiny | grpo | agentic | bimodal | long | long_control")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--gather-bwd", action="store_true",
+                    help="also time the gather backward (d logits) after the gather, reported "
+                         "under kernels; it stays out of value (the wall-clock ms_per_step then "
+                         "includes it)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
@@ -154,13 +158,18 @@ def main():
         b["logits"] = forest_tensor((w.vocab,), "logits", std=w.logit_std)
         b["lp"] = torch.empty(n_out_all, dtype=torch.float32, device=dev)
         b["ent"] = torch.empty(n_out_all, dtype=torch.float32, device=dev)
+        if args.gather_bwd:
+            gen = torch.Generator(device=dev).manual_seed(w.seed + 99)
+            b["dlp"] = torch.randn(n_out_all, generator=gen, device=dev)
+            b["dent"] = torch.randn(n_out_all, generator=gen, device=dev)
+            b["dlogits"] = torch.empty_like(b["logits"])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def step(record):
         forest = pst.build_tree(w.seqs, w.max_tokens_per_mb)
         m = pst.forest_meta_create(forest, stream)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if record else None
         if record:
             e[0].record(stream)
         pst.tree_attn_fwd(b["q"], b["k"], b["v"], m, out=b["o"], lse=b["lse"], stream=stream)
@@ -176,6 +185,14 @@ def main():
                                              stream=stream)
         if record:
             e[3].record(stream)
+        if w.gather and args.gather_bwd:
+            # outside the timed path of the step (its own event pair)
+            if record:
+                e[4].record(stream)
+            pst.gather_tree_logprobs_entropy_bwd(b["logits"], m, b["dlp"], b["dent"],
+                                                 dlogits=b["dlogits"], stream=stream)
+            if record:
+                e[5].record(stream)
         return forest, [m], [e] if record else []
 
     def release(items):
@@ -203,12 +220,14 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) / args.steps * 1e3
 
-    fwd_ms, bwd_ms, gat_ms = [], [], []
+    fwd_ms, bwd_ms, gat_ms, gbw_ms = [], [], [], []
     for _, _, evs in done:
         for e in evs:
             fwd_ms.append(e[0].elapsed_time(e[1]))
             bwd_ms.append(e[1].elapsed_time(e[2]))
             gat_ms.append(e[2].elapsed_time(e[3]))
+            if w.gather and args.gather_bwd:
+                gbw_ms.append(e[4].elapsed_time(e[5]))
     release(done)
 
     K = args.steps
@@ -234,6 +253,13 @@ def main():
         gather_bytes = n_real * w.vocab * esz + n_out * (4 + 4 + 4 + 4) + 4 * (Np_all + 1)
         kernels["gather"] = {"ms_per_step": gat_t * 1e3, "GB/s": gather_bytes / gat_t / 1e9,
                              "launches_per_step": 1}
+        if args.gather_bwd:
+            gbw_t = sum(gbw_ms) / K * 1e-3
+            # real rows read once + every row of d logits written + per output
+            # its two gradients, slot and target
+            gbw_bytes = (n_real + Np_all) * w.vocab * esz + n_out * 16 + 4 * (Np_all + 1)
+            kernels["gather_bwd"] = {"ms_per_step": gbw_t * 1e3, "GB/s": gbw_bytes / gbw_t / 1e9,
+                                     "launches_per_step": 1, "in_step": False}
 
     # roofline of the kernel that takes the most time
     cands = [("attn_fwd", fwd_t), ("attn_bwd", bwd_t), ("gather", gat_t)]

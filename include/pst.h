@@ -225,6 +225,25 @@ int pst_gather_tree_logprobs_entropy(const void* logits, int64_t vocab, int32_t 
                                      const pst_tree_meta* meta, float* logprobs,
                                      float* entropy, void* stream);
 
+/* Gradient of the gather: d logits of
+ *   sum_k dlogprobs[k] * logprobs[k] + dentropy[k] * entropy[k]
+ * with logprobs/entropy as pst_gather_tree_logprobs_entropy defines them
+ * (the loss path the "对数概率计算" section feeds).  For a row x serving
+ * outputs k (next token t_k, none at a sequence's last position):
+ *   dx_v = -p_v (A + B (log p_v + H)) + sum_{k: t_k = v} dlogprobs[k],
+ *   A = sum over outputs with a next token of dlogprobs, B = sum of dentropy,
+ * p = softmax(x), H its entropy (a zero probability contributes 0).  Each
+ * real row is read twice (statistics, then gradient) and written once; rows
+ * no output reads (pad rows) are written as zeros.  Deterministic.
+ *   logits     device [Np, vocab] dtype
+ *   dlogprobs  device float32 [n_out], dentropy device float32 [n_out]
+ *   dlogits    device [Np, vocab] dtype (written), same alignment as logits
+ *              modulo 16 bytes
+ * Errors: PST_EINVAL, PST_EDTYPE, PST_ESHAPE, PST_EHIP. */
+int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int32_t dtype,
+                                         const pst_tree_meta* meta, const float* dlogprobs,
+                                         const float* dentropy, void* dlogits, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* pst_last_error(void);
 

@@ -64,12 +64,21 @@ def gather_logprobs_entropy(tree: Tree, seqs, logits):
     return np.concatenate(outs_lp), np.concatenate(outs_h)
 
 
-def gather_logprobs_entropy_bwd(tree: Tree, seqs, logits, dlogprobs, dentropy):
+def gather_logprobs_entropy_bwd(tree: Tree, seqs, logits, dlogprobs, dentropy, rows=None):
     """Gradient of sum(dlogprobs * logprobs + dentropy * entropy) with respect
     to the logits [Np, V] of one tree, where logprobs/entropy are
-    gather_logprobs_entropy(tree, seqs, logits).  Returns float64 [Np, V]."""
-    x_all = np.asarray(logits, dtype=np.float64)
-    grad = np.zeros_like(x_all)
+    gather_logprobs_entropy(tree, seqs, logits).  Returns float64 [Np, V].
+
+    With `rows` (a collection of row indices), `logits` maps each of those
+    rows to its logits and only their gradients are formed: a dict row ->
+    float64 [V] (for trees whose full logits do not fit the host)."""
+    if rows is None:
+        x_all = np.asarray(logits, dtype=np.float64)
+        grad = np.zeros_like(x_all)
+        want = None
+    else:
+        want = set(int(r) for r in rows)
+        grad = {r: np.zeros(len(logits[r])) for r in want}
     dlp = np.asarray(dlogprobs, dtype=np.float64)
     dh = np.asarray(dentropy, dtype=np.float64)
     off = 0
@@ -78,7 +87,9 @@ def gather_logprobs_entropy_bwd(tree: Tree, seqs, logits, dlogprobs, dentropy):
         idx = tree.seq_index[sid]
         for t in range(len(seq)):
             row = int(idx[t])
-            x = x_all[row]
+            if want is not None and row not in want:
+                continue
+            x = np.asarray(logits[row], dtype=np.float64) if want is not None else x_all[row]
             m = x.max()
             e = np.exp(x - m)
             z = e.sum()

@@ -73,6 +73,8 @@ _SIGS = {
                                     c_int32, c_int32, c_int32, c_int32, c_float, c_void_p]),
     "pst_gather_tree_logprobs_entropy": (c_int32, [c_void_p, c_int64, c_int32, c_void_p,
                                                    c_void_p, c_void_p, c_void_p]),
+    "pst_gather_tree_logprobs_entropy_bwd": (c_int32, [c_void_p, c_int64, c_int32, c_void_p,
+                                                       c_void_p, c_void_p, c_void_p, c_void_p]),
     "pst_last_error": (c_char_p, []),
 }
 

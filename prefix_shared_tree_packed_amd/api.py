@@ -237,3 +237,26 @@ def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=
         _dev_tensor(logprobs, "logprobs").data_ptr(), _dev_tensor(entropy, "entropy").data_ptr(),
         c_void_p(_stream_ptr(stream))))
     return logprobs, entropy
+
+
+def gather_tree_logprobs_entropy_bwd(logits, meta: TreeMeta, dlogprobs, dentropy, dlogits=None,
+                                     stream=None):
+    """d logits of sum(dlogprobs * logprobs + dentropy * entropy); returns
+    dlogits [Np, V] in the logits' dtype (pad rows zero)."""
+    import torch
+    _dev_tensor(logits, "logits")
+    if logits.dim() != 2 or logits.shape[0] != meta.n_padded:
+        raise ValueError(f"logits must be [{meta.n_padded}, V], got {tuple(logits.shape)}")
+    for t, name in ((dlogprobs, "dlogprobs"), (dentropy, "dentropy")):
+        _dev_tensor(t, name)
+        if t.dtype != torch.float32 or t.numel() != meta.n_out:
+            raise ValueError(f"{name} must be float32 [{meta.n_out}]")
+    if dlogits is None:
+        dlogits = torch.empty_like(logits)
+    elif dlogits.shape != logits.shape or dlogits.dtype != logits.dtype:
+        raise ValueError("dlogits must match logits in shape and dtype")
+    check(_lib.load().pst_gather_tree_logprobs_entropy_bwd(
+        logits.data_ptr(), int(logits.shape[1]), _dtype_code(logits), meta._h,
+        dlogprobs.data_ptr(), dentropy.data_ptr(), _dev_tensor(dlogits, "dlogits").data_ptr(),
+        c_void_p(_stream_ptr(stream))))
+    return dlogits

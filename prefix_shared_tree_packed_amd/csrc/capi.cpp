@@ -460,4 +460,29 @@ int pst_gather_tree_logprobs_entropy(const void* logits, int64_t vocab, int32_t 
   return ok();
 }
 
+int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int32_t dtype,
+                                         const pst_tree_meta* meta, const float* dlogprobs,
+                                         const float* dentropy, void* dlogits, void* stream) {
+  if (!meta) return fail(PST_EINVAL, "tree metadata is NULL");
+  if (dtype != PST_F32 && dtype != PST_BF16)
+    return fail(PST_EDTYPE, "unknown dtype " + std::to_string(dtype));
+  if (vocab <= 0) return fail(PST_EINVAL, "vocab must be positive");
+  if (meta->max_target >= vocab || meta->min_target < 0)
+    return fail(PST_EINVAL, "next-token ids span [" + std::to_string(meta->min_target) + ", " +
+                                std::to_string(meta->max_target) + "], outside the vocab of " +
+                                std::to_string(vocab));
+  if (!logits || !dlogprobs || !dentropy || !dlogits)
+    return fail(PST_EINVAL, "NULL device pointer");
+  const size_t esz = dtype == PST_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(logits) % esz || reinterpret_cast<uintptr_t>(dlogits) % esz)
+    return fail(PST_ESHAPE, "logits or dlogits pointer is not aligned to its element size");
+  if ((reinterpret_cast<uintptr_t>(logits) - reinterpret_cast<uintptr_t>(dlogits)) % 16)
+    return fail(PST_ESHAPE, "logits and dlogits must share their alignment modulo 16 bytes");
+  if (int e = check_meta_device(meta)) return e;
+  const hipError_t e = pst::launch_gather_bwd(dtype, logits, vocab, meta->dev, dlogprobs, dentropy,
+                                              dlogits, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather backward launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -42,4 +42,9 @@ hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v
 hipError_t launch_gather(int dtype, const void* logits, int64_t vocab, const TreeDev& tr,
                          float* logprobs, float* entropy, hipStream_t stream);
 
+// dlogits [Np, vocab] (dtype) from dlogprobs / dentropy (float32 [n_out]).
+hipError_t launch_gather_bwd(int dtype, const void* logits, int64_t vocab, const TreeDev& tr,
+                             const float* dlogprobs, const float* dentropy, void* dlogits,
+                             hipStream_t stream);
+
 }  // namespace pst

@@ -4,6 +4,7 @@
    (log_softmax + gather, entropy from softmax), rows read through the index
    maps, gives the same gradient with respect to the packed logits;
  * central finite differences of the oracle's own forward agree;
+ * the row-subset form equals the full form on the rows it is asked for;
  * closed forms: with uniform logits the entropy gradient vanishes
    (log p + H = 0) and a single logprob gradient g gives g (e_target - 1/V);
    pad rows and the last position of each sequence contribute nothing.
@@ -111,3 +112,18 @@ def test_bwd_closed_forms():
     g = oracle.gather_logprobs_entropy_bwd(tree, seqs, logits, dlp, np.zeros(n))
     assert not g.any()
     assert math.isclose(float(np.log(V)), float(oracle.row_lse_entropy(logits[:1])[1][0]), rel_tol=1e-12)
+
+
+def test_bwd_rows_subset_matches_full():
+    rng = np.random.default_rng(5)
+    seqs = _seqs(rng, 11)
+    tree = oracle.build_forest(seqs, 128).trees[0]
+    logits = rng.normal(0, 1.5, size=(tree.n_padded, 11))
+    n = int(tree.out_offsets[-1])
+    dlp, dh = rng.normal(size=n), rng.normal(size=n)
+    full = oracle.gather_logprobs_entropy_bwd(tree, seqs, logits, dlp, dh)
+    rows = [0, 3, tree.n_tokens - 1, tree.n_padded - 1]
+    sub = oracle.gather_logprobs_entropy_bwd(tree, seqs, {r: logits[r] for r in rows}, dlp, dh,
+                                             rows=rows)
+    for r in rows:
+        assert np.array_equal(sub[r], full[r])
