@@ -15,6 +15,7 @@ Modules:
   gather      per-sequence next-token log-probabilities and entropies, and
               their gradient with respect to the packed logits
   accounting  tree_token_ratio, visible pairs, FLOP counts
+  rope        rotary position embedding with pos = depth
 """
 
 from .tree import (  # noqa: F401
@@ -28,3 +29,4 @@ from .gather import (  # noqa: F401
     gather_logprobs_entropy, gather_logprobs_entropy_bwd, row_lse_entropy,
 )
 from .accounting import forest_stats  # noqa: F401
+from .rope import rope  # noqa: F401
