@@ -244,6 +244,23 @@ int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int3
                                          const pst_tree_meta* meta, const float* dlogprobs,
                                          const float* dentropy, void* dlogits, void* stream);
 
+/* ---- device: tree-position rotary embedding -------------------------------- */
+
+/* Rotary position embedding of packed tokens, in place, with position =
+ * depth in the trie (the position the token has in every sequence through
+ * it: TrieNode / "树构建过程" step 4, the position_ids the model receives).
+ * For each row, head and i < head_dim/2, dims i and i + head_dim/2 are
+ * rotated by a = pos * theta^(-2i/head_dim) (rotate-half pairing):
+ *   y_i = x_i cos a - x_{i+d/2} sin a,   y_{i+d/2} = x_{i+d/2} cos a + x_i sin a
+ * inverse != 0 rotates by -a (the backward of the forward rotation).  Angles
+ * are formed in float64; pad rows are left untouched (position 0).
+ *   x   device [Np, n_heads, head_dim] dtype, 16-byte aligned (read and written)
+ * theta <= 0 selects 10000.  head_dim: a multiple of 16 (bf16) or 8 (fp32),
+ * at most 256.
+ * Errors: PST_EINVAL, PST_EDTYPE, PST_ESHAPE, PST_EHIP. */
+int pst_tree_rope(void* x, const pst_tree_meta* meta, int32_t n_heads, int32_t head_dim,
+                  int32_t dtype, float theta, int32_t inverse, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* pst_last_error(void);
 

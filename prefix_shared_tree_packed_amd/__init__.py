@@ -17,4 +17,5 @@ from .api import (  # noqa: F401
     tree_attn_bwd_workspace_bytes,
     gather_tree_logprobs_entropy,
     gather_tree_logprobs_entropy_bwd,
+    tree_rope,
 )

@@ -75,6 +75,8 @@ _SIGS = {
                                                    c_void_p, c_void_p, c_void_p]),
     "pst_gather_tree_logprobs_entropy_bwd": (c_int32, [c_void_p, c_int64, c_int32, c_void_p,
                                                        c_void_p, c_void_p, c_void_p, c_void_p]),
+    "pst_tree_rope": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float, c_int32,
+                                c_void_p]),
     "pst_last_error": (c_char_p, []),
 }
 

@@ -260,3 +260,15 @@ def gather_tree_logprobs_entropy_bwd(logits, meta: TreeMeta, dlogprobs, dentropy
         dlogprobs.data_ptr(), dentropy.data_ptr(), _dev_tensor(dlogits, "dlogits").data_ptr(),
         c_void_p(_stream_ptr(stream))))
     return dlogits
+
+
+def tree_rope(x, meta: TreeMeta, theta: Optional[float] = None, inverse: bool = False, stream=None):
+    """Rotary embedding of packed x [Np, heads, head_dim] in place with
+    position = depth (inverse: the backward rotation); returns x."""
+    _dev_tensor(x, "x")
+    if x.dim() != 3 or x.shape[0] != meta.n_padded:
+        raise ValueError(f"x must be [{meta.n_padded}, heads, head_dim], got {tuple(x.shape)}")
+    check(_lib.load().pst_tree_rope(
+        x.data_ptr(), meta._h, int(x.shape[1]), int(x.shape[2]), _dtype_code(x),
+        float(theta or 0.0), int(bool(inverse)), c_void_p(_stream_ptr(stream))))
+    return x

@@ -39,6 +39,7 @@ HIP_SOURCES = [
     "kernels/attn_bwd.hip",
     "kernels/attn_bwd_bf16.hip",
     "kernels/gather.hip",
+    "kernels/rope.hip",
 ]
 CXX_SOURCES = ["host/forest.cpp"]
 

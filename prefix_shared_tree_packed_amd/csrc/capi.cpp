@@ -23,8 +23,9 @@ struct pst_forest {
 // se [Np] | q_ptr [nb+1] | q_tile [n_tiles] | kb_qhi [nb] | fwd_order [nb] |
 // bwd_order [nb] | row_out_ptr [Np+1] | out_pos [n_out] | out_tgt [n_out] |
 // blk32 [Np/32][2] (min, max subtree end of each 32-key block) |
-// q_cls [n_tiles] (32x32 sub-block classes of each tile), every
-// section starting on a 16-byte boundary.  The pinned staging copy is
+// q_cls [n_tiles] (32x32 sub-block classes of each tile) | pos [Np] (depth
+// of every row, 0 for pad rows), every section starting on a 16-byte
+// boundary.  The pinned staging copy is
 // kept until destroy so the asynchronous upload never reads freed memory.
 struct pst_tree_meta {
   int device = -1;
@@ -164,6 +165,7 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   const size_t o_otgt = off;      off += round4(n_out);
   const size_t o_blk = off;       off += round4(Np / 16);
   const size_t o_qcls = off;      off += round4(n_tiles);
+  const size_t o_pos = off;       off += round4(Np);
   const size_t words = off;
 
   pst_tree_meta* m = new (std::nothrow) pst_tree_meta;
@@ -191,6 +193,7 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   for (const pst::Tree* tp : trees) {
     const pst::Tree& t = *tp;
     for (int32_t i = 0; i < t.Np; ++i) h[o_se + row0 + i] = t.se[i] + row0;
+    for (int32_t i = 0; i < t.Np; ++i) h[o_pos + row0 + i] = t.pos[i];
     for (int32_t qb = 0; qb < t.nb; ++qb) h[o_qptr + blk0 + qb] = tile0 + t.q_ptr[qb];
     for (int32_t i = 0; i < t.n_tiles(); ++i) {
       h[o_qtile + tile0 + i] = ((t.q_kb[i] + blk0) << 1) | (t.q_full[i] & 1);
@@ -249,7 +252,7 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   int32_t* d = m->dbuf;
   m->dev = pst::TreeDev{d + o_se,   d + o_qptr, d + o_qtile, d + o_qhi,  d + o_ford,
                         d + o_bord, d + o_rptr, d + o_opos,  d + o_otgt, d + o_blk, d + o_qcls,
-                        sz.n_tokens, sz.n_padded, sz.n_blocks, sz.n_tiles};
+                        d + o_pos,  sz.n_tokens, sz.n_padded, sz.n_blocks, sz.n_tiles};
   *out = m;
   return ok();
 }
@@ -482,6 +485,25 @@ int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int3
   const hipError_t e = pst::launch_gather_bwd(dtype, logits, vocab, meta->dev, dlogprobs, dentropy,
                                               dlogits, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gather backward launch");
+  return ok();
+}
+
+int pst_tree_rope(void* x, const pst_tree_meta* meta, int32_t n_heads, int32_t head_dim,
+                  int32_t dtype, float theta, int32_t inverse, void* stream) {
+  if (!meta) return fail(PST_EINVAL, "tree metadata is NULL");
+  if (dtype != PST_F32 && dtype != PST_BF16)
+    return fail(PST_EDTYPE, "unknown dtype " + std::to_string(dtype));
+  if (n_heads <= 0) return fail(PST_ESHAPE, "n_heads must be positive");
+  const int unit = dtype == PST_BF16 ? 16 : 8;  // two 16-byte chunks per dim pair half
+  if (head_dim <= 0 || head_dim > 256 || head_dim % unit)
+    return fail(PST_ESHAPE, "head_dim must be a multiple of " + std::to_string(unit) +
+                                " in (0, 256], got " + std::to_string(head_dim));
+  if (int e = check_ptrs({x}, "x")) return e;
+  if (int e = check_meta_device(meta)) return e;
+  const hipError_t e = pst::launch_rope(dtype, x, meta->dev, n_heads, head_dim,
+                                        theta > 0.f ? theta : 10000.f, inverse != 0,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope launch");
   return ok();
 }
 

@@ -36,6 +36,7 @@ struct TreeDev {
   const int32_t* q_cls;        // [n_tiles] 2-bit class of each 32x32 sub-block (query
                                // sub-block qs, key sub-block ks at bit 2*(4*qs+ks)):
                                // 0 no visible pair, 1 some, 2 all
+  const int32_t* pos;          // [Np] depth of every row (position id), 0 for pad rows
   int32_t N;
   int32_t Np;
   int32_t nb;

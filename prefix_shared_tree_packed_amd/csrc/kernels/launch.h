@@ -47,4 +47,9 @@ hipError_t launch_gather_bwd(int dtype, const void* logits, int64_t vocab, const
                              const float* dlogprobs, const float* dentropy, void* dlogits,
                              hipStream_t stream);
 
+// In-place rotary embedding of x [Np, heads, head_dim] with pos = depth
+// (inverse: the opposite rotation, the backward).
+hipError_t launch_rope(int dtype, void* x, const TreeDev& tr, int heads, int head_dim,
+                       float theta, bool inverse, hipStream_t stream);
+
 }  // namespace pst

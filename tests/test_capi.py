@@ -31,6 +31,8 @@ def test_device_entry_points_reject_null_meta():
     assert b"NULL" in lib.pst_last_error()
     rc = lib.pst_gather_tree_logprobs_entropy_bwd(p, 100, 1, None, p, p, p, None)
     assert _lib.ERRORS[rc] == "PST_EINVAL"
+    rc = lib.pst_tree_rope(p, None, 8, 128, 1, 0.0, 0, None)
+    assert _lib.ERRORS[rc] == "PST_EINVAL"
 
 
 def test_meta_create_rejects_bad_tree_index():
