@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--workload", default="grpo",
                     help="tiny | grpo | agentic | bimodal | long | long_control")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--rope", action="store_true",
+                    help="also time the tree-position rotary embedding of Q and K (in place), "
+                         "reported under kernels; it stays out of value")
     ap.add_argument("--gather-bwd", action="store_true",
                     help="also time the gather backward (d logits) after the gather, reported "
                          "under kernels; it stays out of value (the wall-clock ms_per_step then "
@@ -169,7 +172,7 @@ def main():
     def step(record):
         forest = pst.build_tree(w.seqs, w.max_tokens_per_mb)
         m = pst.forest_meta_create(forest, stream)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if record else None
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(8)] if record else None
         if record:
             e[0].record(stream)
         pst.tree_attn_fwd(b["q"], b["k"], b["v"], m, out=b["o"], lse=b["lse"], stream=stream)
@@ -185,6 +188,13 @@ def main():
                                              stream=stream)
         if record:
             e[3].record(stream)
+        if args.rope:
+            if record:
+                e[6].record(stream)
+            pst.tree_rope(b["q"], m, stream=stream)
+            pst.tree_rope(b["k"], m, stream=stream)
+            if record:
+                e[7].record(stream)
         if w.gather and args.gather_bwd:
             # outside the timed path of the step (its own event pair)
             if record:
@@ -220,7 +230,7 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) / args.steps * 1e3
 
-    fwd_ms, bwd_ms, gat_ms, gbw_ms = [], [], [], []
+    fwd_ms, bwd_ms, gat_ms, gbw_ms, rope_ms = [], [], [], [], []
     for _, _, evs in done:
         for e in evs:
             fwd_ms.append(e[0].elapsed_time(e[1]))
@@ -228,6 +238,8 @@ def main():
             gat_ms.append(e[2].elapsed_time(e[3]))
             if w.gather and args.gather_bwd:
                 gbw_ms.append(e[4].elapsed_time(e[5]))
+            if args.rope:
+                rope_ms.append(e[6].elapsed_time(e[7]))
     release(done)
 
     K = args.steps
@@ -243,6 +255,13 @@ def main():
     if w.bwd:
         kernels["attn_bwd"] = {"ms_per_step": bwd_t * 1e3, "TFLOP/s": bwd_flops / bwd_t / 1e12,
                                "launches_per_step": 1}
+    if args.rope:
+        rope_t = sum(rope_ms) / K * 1e-3
+        esz_qk = 4 if w.dtype == "f32" else 2
+        # real rows of Q and K read and written once, the row pointers and depths
+        rope_bytes = 2 * stats["tree_tokens"] * (hq + hkv) * d * esz_qk + 2 * 2 * 4 * (Np_all + 1)
+        kernels["rope_qk"] = {"ms_per_step": rope_t * 1e3, "GB/s": rope_bytes / rope_t / 1e9,
+                              "launches_per_step": 2, "in_step": False}
     gather_bytes = 0
     if w.gather:
         esz = 4 if w.dtype == "f32" else 2

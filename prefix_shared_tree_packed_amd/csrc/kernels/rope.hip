@@ -7,10 +7,13 @@
 // backward (gradient of the output with respect to the input, applied to the
 // output gradient).
 //
-// One 256-thread workgroup per row.  The row's d/2 angles are formed once in
-// float64 (exact power, reduction modulo 2 pi, sin/cos) and shared through
-// LDS by all heads; each thread then rotates 16-byte chunks of one dim-pair
-// half and its partner.  Pad rows are skipped (position 0: the identity).
+// One 256-thread workgroup per four rows.  Each row's d/2 angles are formed
+// once: the powers theta^(-2i/d) in float64 on the host, the product with
+// the position and its reduction modulo 2 pi in float64 on the device, then
+// float sin/cos of the reduced angle; they are shared through LDS by all
+// heads; each thread then rotates 16-byte chunks of one
+// dim-pair half and its partner.  Pad rows are skipped (position 0: the
+// identity).
 // HBM-bound: the tensor is read and written once.
 #include "launch.h"
 
@@ -54,28 +57,47 @@ struct Vec<float> {
   }
 };
 
+constexpr int kRows = 4;  // rows per workgroup
+
+// theta^(-2i/d) for i < d/2, formed on the host in double precision
+struct InvFreq {
+  double f[kTile];
+};
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, TreeDev tr, int heads,
-                                                        int d, double theta, float sign) {
+                                                        int d, InvFreq inv, float sign) {
   constexpr int E = Vec<T>::E;
-  __shared__ float cs[2][kTile];  // cos, sin of the row's d/2 angles (d <= 256)
-  const int row = blockIdx.x;
-  if (tr.row_out_ptr[row] == tr.row_out_ptr[row + 1]) return;  // a pad row: position 0
+  __shared__ float cs[kRows][2][kTile];  // cos, sin of each row's d/2 angles (d <= 256)
+  const int row0 = blockIdx.x * kRows;
   const int half = d / 2;
   const int tid = threadIdx.x;
-  if (tid < half) {
-    const double a = static_cast<double>(tr.pos[row]) * pow(theta, -2.0 * tid / d);
-    const double r = fmod(a, 6.283185307179586476925286766559);
-    cs[0][tid] = static_cast<float>(cos(r));
-    cs[1][tid] = sign * static_cast<float>(sin(r));
+  for (int k = tid; k < kRows * half; k += kThreads) {
+    const int r = k / half, i = k - r * half;
+    const int row = row0 + r;
+    // the angle in double, reduced to [0, 2 pi) there; float sin/cos of
+    // the reduced angle are then accurate to float rounding
+    constexpr double kTwoPi = 6.283185307179586476925286766559;
+    const double a = row < tr.Np ? static_cast<double>(tr.pos[row]) * inv.f[i] : 0.0;
+    const float red = static_cast<float>(a - kTwoPi * floor(a / kTwoPi));
+    float sn, cn;
+    sincosf(red, &sn, &cn);
+    cs[r][0][i] = cn;
+    cs[r][1][i] = sign * sn;
   }
   __syncthreads();
-  // chunk c of the row: head c / (half / E), dims (c % (half / E)) * E ..
+  // chunk c of a row: head c / (half / E), dims (c % (half / E)) * E ..
   const int cph = half / E;  // chunks per pair half of one head
-  T* xr = x + static_cast<size_t>(row) * heads * d;
-  for (int c = tid; c < heads * cph; c += kThreads) {
-    const int h = c / cph;
-    const int i0 = (c - h * cph) * E;
+  const int per_row = heads * cph;
+  for (int c = tid; c < kRows * per_row; c += kThreads) {
+    const int r = c / per_row;
+    const int row = row0 + r;
+    // rows past the end and pad rows (position 0: the identity) are skipped
+    if (row >= tr.Np || tr.row_out_ptr[row] == tr.row_out_ptr[row + 1]) continue;
+    const int cr = c - r * per_row;
+    const int h = cr / cph;
+    const int i0 = (cr - h * cph) * E;
+    T* xr = x + static_cast<size_t>(row) * heads * d;
     uint4* p1 = reinterpret_cast<uint4*>(xr + h * d + i0);
     uint4* p2 = reinterpret_cast<uint4*>(xr + h * d + half + i0);
     float a[E], b[E], ya[E], yb[E];
@@ -83,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, TreeD
     Vec<T>::unpack(*p2, b);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const float co = cs[0][i0 + e], si = cs[1][i0 + e];
+      const float co = cs[r][0][i0 + e], si = cs[r][1][i0 + e];
       ya[e] = a[e] * co - b[e] * si;
       yb[e] = b[e] * co + a[e] * si;
     }
@@ -97,14 +119,17 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, TreeD
 hipError_t launch_rope(int dtype, void* x, const TreeDev& tr, int heads, int head_dim,
                        float theta, bool inverse, hipStream_t stream) {
   if (tr.Np == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(tr.Np));
+  const dim3 grid(static_cast<unsigned>((tr.Np + kRows - 1) / kRows));
   const float sign = inverse ? -1.f : 1.f;
+  InvFreq inv{};
+  for (int i = 0; i < head_dim / 2; ++i)
+    inv.f[i] = std::pow(static_cast<double>(theta), -2.0 * i / head_dim);
   if (dtype == kDtypeBf16)
     hipLaunchKernelGGL(rope_kernel<bf16_t>, grid, dim3(kThreads), 0, stream, static_cast<bf16_t*>(x),
-                       tr, heads, head_dim, static_cast<double>(theta), sign);
+                       tr, heads, head_dim, inv, sign);
   else
     hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(kThreads), 0, stream, static_cast<float*>(x),
-                       tr, heads, head_dim, static_cast<double>(theta), sign);
+                       tr, heads, head_dim, inv, sign);
   return hipGetLastError();
 }
 
