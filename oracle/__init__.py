@@ -16,6 +16,9 @@ Modules:
               their gradient with respect to the packed logits
   accounting  tree_token_ratio, visible pairs, FLOP counts
   rope        rotary position embedding with pos = depth
+  packing     FFD and Karmarkar-Karp allocation of items (sequences, trees)
+              to micro-batches or ranks, and the packing-quality metrics
+              (from the article on AReaL's FFD/KK packing)
 """
 
 from .tree import (  # noqa: F401
@@ -30,3 +33,4 @@ from .gather import (  # noqa: F401
 )
 from .accounting import forest_stats  # noqa: F401
 from .rope import rope  # noqa: F401
+from . import packing  # noqa: F401
