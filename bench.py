@@ -331,6 +331,8 @@ def main():
         "cpu_baseline": None,
     }
 
+    out["host_packing"] = host_packing(pst, w, shape_forest)
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device=dev)
@@ -346,6 +348,38 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, sizes, b, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def host_packing(pst, w, forest, ranks=8, reps=5):
+    """Host allocation timings: the workload's sequence lengths into
+    micro-batches of its capacity (FFD and KK, with KK's fallback flag), the
+    same lengths balanced over `ranks` ranks, and the trees balanced over the
+    ranks by visible pairs; best of `reps` runs each, with the spread."""
+    import numpy as np
+    lens = np.array([len(s) for s in w.seqs], dtype=np.int64)
+    res = {"items": int(lens.size), "ranks": ranks}
+
+    def timed(fn):
+        best, r = float("inf"), None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            r = fn()
+            best = min(best, time.perf_counter() - t0)
+        return r, best * 1e3
+
+    for alg in ("ffd", "kk"):
+        (g, fb), ms = timed(lambda: pst.pack_allocate(lens, w.max_tokens_per_mb, 1, 1, alg))
+        m = pst.packing_metrics(lens, g, w.max_tokens_per_mb)
+        res[f"mb_{alg}"] = {"ms": ms, "groups": len(g), "fell_back": fb, "spread": m["spread"],
+                            "utilization": m["utilization"]}
+        (g, fb), ms = timed(lambda: pst.pack_allocate(lens, 1 << 62, ranks, 1, alg))
+        m = pst.packing_metrics(lens, g, 1 << 62)
+        res[f"ranks_{alg}"] = {"ms": ms, "spread": m["spread"], "imbalance_ratio": m["imbalance_ratio"]}
+        rank, ms = timed(lambda: pst.assign_trees(forest, ranks, cost="pairs", algorithm=alg))
+        pairs = np.array([forest.sizes(t)["n_pairs"] for t in range(forest.n_trees)])
+        loads = np.bincount(rank, weights=pairs, minlength=ranks)
+        res[f"trees_{alg}"] = {"ms": ms, "max_pairs": int(loads.max()), "min_pairs": int(loads.min())}
+    return res
 
 
 def cpu_model():

@@ -253,13 +253,68 @@ int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int3
  * rotated by a = pos * theta^(-2i/head_dim) (rotate-half pairing):
  *   y_i = x_i cos a - x_{i+d/2} sin a,   y_{i+d/2} = x_{i+d/2} cos a + x_i sin a
  * inverse != 0 rotates by -a (the backward of the forward rotation).  Angles
- * are formed in float64; pad rows are left untouched (position 0).
+ * are formed and reduced modulo 2 pi in float64, their sine and cosine taken
+ * in float; pad rows are left untouched (position 0).
  *   x   device [Np, n_heads, head_dim] dtype, 16-byte aligned (read and written)
  * theta <= 0 selects 10000.  head_dim: a multiple of 16 (bf16) or 8 (fp32),
  * at most 256.
  * Errors: PST_EINVAL, PST_EDTYPE, PST_ESHAPE, PST_EHIP. */
 int pst_tree_rope(void* x, const pst_tree_meta* meta, int32_t n_heads, int32_t head_dim,
                   int32_t dtype, float theta, int32_t inverse, void* stream);
+
+/* ---- host: micro-batch / rank allocation -------------------------------- */
+
+/* Packing algorithms (article on AReaL's FFD/KK micro-batch packing). */
+enum { PST_PACK_FFD = 0, PST_PACK_KK = 1 };
+
+typedef struct {
+  int32_t n_groups;
+  int64_t total;          /* sum of all values */
+  int64_t max_load;       /* largest group sum */
+  int64_t min_load;       /* smallest group sum */
+  int64_t spread;         /* max_load - min_load */
+  int64_t wasted_tokens;  /* n_groups * capacity - total */
+  double imbalance_ratio; /* max_load / mean (1 when the mean is 0) */
+  double std_dev;         /* population standard deviation of the group sums */
+  double cv;              /* std_dev / mean (0 when the mean is 0) */
+  double utilization;     /* total / (n_groups * capacity) */
+} pst_pack_metrics;
+
+/* Allocate n weighted items (sequence lengths, per-tree costs) to groups
+ * (micro-batches, data-parallel ranks), as the packing article's FFD and KK
+ * sections describe.
+ *   values      host int64 [n], non-negative, each at most `capacity`
+ *   capacity    largest group sum allowed (a huge value balances without a
+ *               capacity, as for assigning work to ranks)
+ *   min_groups  at least this many groups (never more groups than items)
+ *   divisor     the group count is rounded up to a multiple of it where the
+ *               item count allows
+ *   algorithm   PST_PACK_FFD: stable descending order, each item to the
+ *               lightest group it fits (lowest index on ties), else a new
+ *               group; the first min_groups items open groups.
+ *               PST_PACK_KK: k-way Karmarkar-Karp largest differencing with
+ *               k = max(min_groups, ceil(total / capacity)) rounded up to the
+ *               divisor and capped at n; states pop by largest spread (push
+ *               order on ties) and combine lightest-with-heaviest subsets.  If
+ *               a group still exceeds the capacity, FFD is used instead.
+ *   group_of    host int32 [n] out: the group of every item; KK numbers its
+ *               groups in ascending order of their sums, FFD in creation order
+ *   n_groups    out: the number of groups
+ *   fell_back   out (may be NULL): 1 when KK fell back to FFD
+ * Errors: PST_EINVAL (NULL, n < 1, capacity <= 0, min_groups or divisor < 1,
+ * negative value, unknown algorithm), PST_ECAPACITY (an item above the
+ * capacity), PST_ENOMEM. */
+int pst_pack_allocate(const int64_t* values, int32_t n, int64_t capacity, int32_t min_groups,
+                      int32_t divisor, int32_t algorithm, int32_t* group_of, int32_t* n_groups,
+                      int32_t* fell_back);
+
+/* Packing-quality metrics of an allocation (the packing article's metrics
+ * section): spread, imbalance ratio, standard deviation, coefficient of
+ * variation, utilization and wasted tokens of the group sums.
+ *   values [n], group_of [n] (each in [0, n_groups)): host arrays.
+ * Errors: PST_EINVAL, PST_ERANGE (a group index out of range). */
+int pst_pack_metrics_compute(const int64_t* values, int32_t n, const int32_t* group_of,
+                             int32_t n_groups, int64_t capacity, pst_pack_metrics* out);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* pst_last_error(void);

@@ -18,4 +18,8 @@ from .api import (  # noqa: F401
     gather_tree_logprobs_entropy,
     gather_tree_logprobs_entropy_bwd,
     tree_rope,
+    PACKING_ALGORITHMS,
+    pack_allocate,
+    packing_metrics,
+    assign_trees,
 )

@@ -52,6 +52,18 @@ class Stats(ctypes.Structure):
     ]
 
 
+PST_PACK_FFD, PST_PACK_KK = 0, 1
+
+
+class PackMetrics(ctypes.Structure):
+    _fields_ = [
+        ("n_groups", c_int32), ("total", c_int64), ("max_load", c_int64),
+        ("min_load", c_int64), ("spread", c_int64), ("wasted_tokens", c_int64),
+        ("imbalance_ratio", c_double), ("std_dev", c_double), ("cv", c_double),
+        ("utilization", c_double),
+    ]
+
+
 _SIGS = {
     "pst_build_tree": (c_int32, [P32, P64, c_int32, c_int32, POINTER(c_void_p)]),
     "pst_forest_num_trees": (c_int32, [c_void_p, P32]),
@@ -77,6 +89,10 @@ _SIGS = {
                                                        c_void_p, c_void_p, c_void_p, c_void_p]),
     "pst_tree_rope": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float, c_int32,
                                 c_void_p]),
+    "pst_pack_allocate": (c_int32, [P64, c_int32, c_int64, c_int32, c_int32, c_int32, P32, P32,
+                                    P32]),
+    "pst_pack_metrics_compute": (c_int32, [P64, c_int32, P32, c_int32, c_int64,
+                                           POINTER(PackMetrics)]),
     "pst_last_error": (c_char_p, []),
 }
 

@@ -6,6 +6,11 @@ every computation happens in the library.  Names follow the C ABI:
     tree_attn_fwd(q, k, v, meta, ...)              -> (o, lse)
     tree_attn_bwd(q, k, v, o, lse, dout, meta, ...) -> (dq, dk, dv)
     gather_tree_logprobs_entropy(logits, meta, ...) -> (logprobs, entropy)
+    gather_tree_logprobs_entropy_bwd(logits, meta, dlogprobs, dentropy) -> dlogits
+    tree_rope(x, meta, theta=None, inverse=False)  -> x rotated in place
+    pack_allocate(values, capacity, ...)           -> (groups, fell_back)   (host)
+    packing_metrics(values, groups, capacity)      -> dict                  (host)
+    assign_trees(forest, n_ranks, ...)             -> rank of every tree    (host)
 """
 
 from __future__ import annotations
@@ -272,3 +277,58 @@ def tree_rope(x, meta: TreeMeta, theta: Optional[float] = None, inverse: bool = 
         x.data_ptr(), meta._h, int(x.shape[1]), int(x.shape[2]), _dtype_code(x),
         float(theta or 0.0), int(bool(inverse)), c_void_p(_stream_ptr(stream))))
     return x
+
+
+PACKING_ALGORITHMS = {"ffd": _lib.PST_PACK_FFD, "kk": _lib.PST_PACK_KK}
+
+
+def pack_allocate(values, capacity: int, min_groups: int = 1, divisor: int = 1,
+                  algorithm: str = "ffd"):
+    """Allocate weighted items to groups with FFD or Karmarkar-Karp (host).
+    Returns (groups, fell_back): groups is a list of item-index lists (items
+    in ascending index), fell_back is True when KK fell back to FFD."""
+    if algorithm not in PACKING_ALGORITHMS:
+        raise ValueError(f"unknown packing algorithm {algorithm!r}; valid: "
+                         + ", ".join(repr(a) for a in PACKING_ALGORITHMS))
+    v = np.ascontiguousarray(values, dtype=np.int64).ravel()
+    group_of = np.zeros(max(v.size, 1), dtype=np.int32)
+    ng, fb = c_int32(), c_int32()
+    check(_lib.load().pst_pack_allocate(
+        v.ctypes.data_as(_lib.P64), v.size, int(capacity), int(min_groups), int(divisor),
+        PACKING_ALGORITHMS[algorithm], group_of.ctypes.data_as(_lib.P32), byref(ng), byref(fb)))
+    groups = [[] for _ in range(ng.value)]
+    for i, g in enumerate(group_of[:v.size]):
+        groups[int(g)].append(i)
+    return groups, bool(fb.value)
+
+
+def packing_metrics(values, groups, capacity: int) -> dict:
+    """Spread, imbalance ratio, std_dev, cv, utilization and wasted tokens of
+    an allocation (groups: lists of item indices covering every item)."""
+    v = np.ascontiguousarray(values, dtype=np.int64).ravel()
+    group_of = np.full(v.size, -1, dtype=np.int32)
+    for g, items in enumerate(groups):
+        group_of[list(items)] = g
+    m = _lib.PackMetrics()
+    check(_lib.load().pst_pack_metrics_compute(
+        v.ctypes.data_as(_lib.P64), v.size, group_of.ctypes.data_as(_lib.P32), len(groups),
+        int(capacity), byref(m)))
+    return {f: getattr(m, f) for f, _ in m._fields_}
+
+
+def assign_trees(forest: Forest, n_ranks: int, cost: str = "pairs", algorithm: str = "kk"):
+    """Balance the trees of a forest over `n_ranks` data-parallel ranks with
+    no capacity limit.  cost: "pairs" (visible attention pairs, the FLOP
+    driver) or "tokens" (real tree tokens).  Returns the rank of every tree
+    (int32 numpy array); with fewer trees than ranks some ranks get none."""
+    key = {"pairs": "n_pairs", "tokens": "n_tokens"}.get(cost)
+    if key is None:
+        raise ValueError(f"unknown cost {cost!r}; valid: 'pairs', 'tokens'")
+    n_trees = forest.stats()["n_trees"]
+    costs = np.array([forest.sizes(t)[key] for t in range(n_trees)], dtype=np.int64)
+    groups, _ = pack_allocate(costs, max(int(costs.sum()), 1), min_groups=n_ranks,
+                              algorithm=algorithm)
+    rank = np.zeros(n_trees, dtype=np.int32)
+    for g, items in enumerate(groups):
+        rank[items] = g
+    return rank

@@ -41,7 +41,7 @@ HIP_SOURCES = [
     "kernels/gather.hip",
     "kernels/rope.hip",
 ]
-CXX_SOURCES = ["host/forest.cpp"]
+CXX_SOURCES = ["host/forest.cpp", "host/packing.cpp"]
 
 
 def _hipcc() -> str:

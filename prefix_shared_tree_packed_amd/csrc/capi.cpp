@@ -13,6 +13,7 @@
 #include <string>
 
 #include "host/forest.h"
+#include "host/packing.h"
 #include "kernels/launch.h"
 
 struct pst_forest {
@@ -260,6 +261,64 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
 }  // namespace
 
 extern "C" {
+
+int pst_pack_allocate(const int64_t* values, int32_t n, int64_t capacity, int32_t min_groups,
+                      int32_t divisor, int32_t algorithm, int32_t* group_of, int32_t* n_groups,
+                      int32_t* fell_back) {
+  if (!values || !group_of || !n_groups) return fail(PST_EINVAL, "NULL argument");
+  if (algorithm != PST_PACK_FFD && algorithm != PST_PACK_KK)
+    return fail(PST_EINVAL, "unknown packing algorithm " + std::to_string(algorithm) +
+                                "; valid: PST_PACK_FFD (0), PST_PACK_KK (1)");
+  if (n < 1) return fail(PST_EINVAL, "no items");
+  if (capacity <= 0) return fail(PST_EINVAL, "capacity must be positive");
+  if (min_groups < 1 || divisor < 1) return fail(PST_EINVAL, "min_groups and divisor must be >= 1");
+  pst::PackResult r;
+  pst::PackStatus st;
+  try {
+    st = algorithm == PST_PACK_KK ? pst::pack_kk(values, n, capacity, min_groups, divisor, &r)
+                                  : pst::pack_ffd(values, n, capacity, min_groups, divisor, &r);
+  } catch (const std::bad_alloc&) {
+    return fail(PST_ENOMEM, "out of host memory while packing");
+  }
+  if (st == pst::kPackCapacity) return fail(PST_ECAPACITY, "an item exceeds the capacity");
+  if (st != pst::kPackOk) return fail(PST_EINVAL, "negative item or item total beyond int64");
+  std::copy(r.group_of.begin(), r.group_of.end(), group_of);
+  *n_groups = r.n_groups;
+  if (fell_back) *fell_back = r.fell_back ? 1 : 0;
+  return ok();
+}
+
+int pst_pack_metrics_compute(const int64_t* values, int32_t n, const int32_t* group_of,
+                             int32_t n_groups, int64_t capacity, pst_pack_metrics* out) {
+  if (!values || !group_of || !out) return fail(PST_EINVAL, "NULL argument");
+  if (n < 1 || n_groups < 1 || capacity <= 0)
+    return fail(PST_EINVAL, "need n >= 1, n_groups >= 1, capacity > 0");
+  std::vector<int64_t> sums(n_groups, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    if (group_of[i] < 0 || group_of[i] >= n_groups)
+      return fail(PST_ERANGE, "group index out of range at item " + std::to_string(i));
+    sums[group_of[i]] += values[i];
+  }
+  int64_t total = 0;
+  for (int64_t v : sums) total += v;
+  const int64_t mx = *std::max_element(sums.begin(), sums.end());
+  const int64_t mn = *std::min_element(sums.begin(), sums.end());
+  const double mean = static_cast<double>(total) / n_groups;
+  double var = 0;
+  for (int64_t v : sums) var += (v - mean) * (v - mean);
+  var /= n_groups;
+  out->n_groups = n_groups;
+  out->total = total;
+  out->max_load = mx;
+  out->min_load = mn;
+  out->spread = mx - mn;
+  out->std_dev = std::sqrt(var);
+  out->imbalance_ratio = mean > 0 ? mx / mean : 1.0;
+  out->cv = mean > 0 ? out->std_dev / mean : 0.0;
+  out->utilization = static_cast<double>(total) / (static_cast<double>(n_groups) * capacity);
+  out->wasted_tokens = static_cast<int64_t>(n_groups) * capacity - total;
+  return ok();
+}
 
 const char* pst_last_error(void) { return g_error.c_str(); }
 

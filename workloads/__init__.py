@@ -13,4 +13,5 @@ from .configs import (  # noqa: F401
     worked_example_edge,
     make_tensor,
     tree_tensor_seed,
+    bimodal_lengths,
 )

@@ -205,6 +205,14 @@ WORKLOADS = {
 }
 
 
+def bimodal_lengths(n: int, seed: int) -> np.ndarray:
+    """Sequence lengths of the packing page's bimodal generator: 70 %
+    U{50..200}, 30 % U{800..2048} (int64 [n])."""
+    rng = np.random.default_rng(seed)
+    long = rng.random(n) < 0.3
+    return np.where(long, rng.integers(800, 2049, size=n), rng.integers(50, 201, size=n)).astype(np.int64)
+
+
 def get_workload(name: str) -> Workload:
     try:
         return WORKLOADS[name]()
