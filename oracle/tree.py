@@ -18,7 +18,9 @@ Readings of points the page leaves open (each the plainest one):
     is a union of whole nodes;
   * the root is virtual (start = end = -1); depth-0 tokens have parent -1;
   * the flattened tree is padded to the next multiple of 128 with pad tokens
-    (id 0, position 0, parent -1) that see only themselves.
+    (id 0, position 0, parent -1) that see only themselves;
+  * pad_to_maximum (configuration section, 启用树训练): every tree is padded
+    to the capacity itself instead, with the same pad tokens.
 
 Everything below is written for clarity: dictionaries for the trie, explicit
 walks of parent chains for the ancestor relation, brute-force scans for the
@@ -169,9 +171,10 @@ def _preorder(root: _TrieTok) -> List[_TrieTok]:
     return out
 
 
-def build_forest(seqs, max_tokens_per_mb: int) -> Forest:
+def build_forest(seqs, max_tokens_per_mb: int, pad_to_maximum: bool = False) -> Forest:
     """Pack `seqs` (sequences of token ids) into compressed, flattened, padded
-    tries of at most `max_tokens_per_mb` tokens each."""
+    tries of at most `max_tokens_per_mb` tokens each.  With pad_to_maximum
+    every tree is padded to max_tokens_per_mb rows."""
     seqs = [np.asarray(s, dtype=np.int64) for s in seqs]
     cap = max_tokens_per_mb
     _validate(seqs, cap)
@@ -200,18 +203,19 @@ def build_forest(seqs, max_tokens_per_mb: int) -> Forest:
     seq_tree = np.full(len(seqs), -1, dtype=np.int32)
     trees = []
     for tid, root in enumerate(tries):
-        trees.append(_flatten(tid, root, seqs, sorted(members[tid])))
+        trees.append(_flatten(tid, root, seqs, sorted(members[tid]),
+                              cap if pad_to_maximum else None))
         for sid in members[tid]:
             seq_tree[sid] = tid
     return Forest(trees, len(seqs), cap, seq_tree)
 
 
-def _flatten(tid: int, root: _TrieTok, seqs, seq_ids: List[int]) -> Tree:
+def _flatten(tid: int, root: _TrieTok, seqs, seq_ids: List[int], pad_to=None) -> Tree:
     toks = _preorder(root)
     N = len(toks)
     for i, t in enumerate(toks):
         t.flat = i
-    Np = -(-N // BLOCK) * BLOCK
+    Np = -(-N // BLOCK) * BLOCK if pad_to is None else pad_to
 
     token = np.zeros(Np, np.int32)
     pos = np.zeros(Np, np.int32)

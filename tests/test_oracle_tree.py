@@ -138,11 +138,12 @@ def _scaled(rng):
     return seqs
 
 
-def _check_invariants(seqs, cap, f):
+def _check_invariants(seqs, cap, f, pad_to_maximum=False):
     seen = []
     for t in f.trees:
         N, Np = t.n_tokens, t.n_padded
-        assert N <= cap and Np % BLOCK == 0 and Np - N < BLOCK and Np <= cap
+        assert N <= cap and Np % BLOCK == 0 and Np <= cap
+        assert Np == cap if pad_to_maximum else Np - N < BLOCK
         seen += t.seq_ids
         # packed tokens <-> distinct non-empty prefixes of the tree's sequences
         prefixes = {}
@@ -239,3 +240,31 @@ def test_brute_force_several_blocks():
         seqs = [s[:cap] for s in seqs]
         f = oracle.build_forest(seqs, cap)
         _check_invariants(seqs, cap, f)
+
+
+def test_pad_to_maximum():
+    """Every tree padded to the capacity: the real part is the default
+    build's, pad rows see only themselves (brute force over the dense mask),
+    and attention of the real rows does not change."""
+    rng = np.random.default_rng(9)
+    for it in range(8):
+        seqs = _scaled(rng) if it % 2 else _random_case(rng)
+        cap = int(rng.choice([256, 384, 512]))
+        seqs = [s[:cap] for s in seqs]
+        f = oracle.build_forest(seqs, cap, pad_to_maximum=True)
+        _check_invariants(seqs, cap, f, pad_to_maximum=True)
+        g = oracle.build_forest(seqs, cap)
+        assert len(f.trees) == len(g.trees)
+        for a, b in zip(f.trees, g.trees):
+            N = b.n_tokens
+            for name in ("token", "pos", "parent", "subtree_end", "node"):
+                assert (getattr(a, name)[:N] == getattr(b, name)[:N]).all(), name
+            assert (a.child_ptr == b.child_ptr).all() and (a.child_idx == b.child_idx).all()
+            assert all((a.seq_index[s] == b.seq_index[s]).all() for s in b.seq_ids)
+            assert a.n_pairs == b.n_pairs
+            q = rng.normal(size=(a.n_padded, 2, 8))
+            k = rng.normal(size=(a.n_padded, 1, 8))
+            v = rng.normal(size=(a.n_padded, 1, 8))
+            oa, la = oracle.attn_fwd(a, q, k, v)
+            ob, lb = oracle.attn_fwd(b, q[:b.n_padded], k[:b.n_padded], v[:b.n_padded])
+            assert np.allclose(oa[:N], ob[:N], rtol=0, atol=1e-12)
