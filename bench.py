@@ -95,6 +95,9 @@ def parse():
                     help="also time the gather backward (d logits) after the gather, reported "
                          "under kernels; it stays out of value (the wall-clock ms_per_step then "
                          "includes it)")
+    ap.add_argument("--mask", action="store_true",
+                    help="also time the dense uint8 mask export of every tree (per-tree metadata, "
+                         "one [Np, Np] buffer reused), reported under kernels; outside the step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
@@ -242,6 +245,11 @@ def main():
                 rope_ms.append(e[6].elapsed_time(e[7]))
     release(done)
 
+    if args.mask:
+        mask_t, mask_bytes = time_dense_mask(pst, torch, shape_forest, sizes, stream, args.steps)
+        mask_entry = {"ms_per_step": mask_t * 1e3, "GB/s": mask_bytes / mask_t / 1e9,
+                      "launches_per_step": n_trees, "in_step": False}
+
     K = args.steps
     pairs = stats["n_pairs"]
     fwd_flops = 4.0 * d * hq * pairs
@@ -262,6 +270,8 @@ def main():
         rope_bytes = 2 * stats["tree_tokens"] * (hq + hkv) * d * esz_qk + 2 * 2 * 4 * (Np_all + 1)
         kernels["rope_qk"] = {"ms_per_step": rope_t * 1e3, "GB/s": rope_bytes / rope_t / 1e9,
                               "launches_per_step": 2, "in_step": False}
+    if args.mask:
+        kernels["dense_mask_u8"] = mask_entry
     gather_bytes = 0
     if w.gather:
         esz = 4 if w.dtype == "f32" else 2
@@ -348,6 +358,32 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, sizes, b, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
+
+
+def time_dense_mask(pst, torch, forest, sizes, stream, steps):
+    """Seconds per pass of the uint8 dense-mask export over every tree, and
+    the algorithmic bytes of a pass (Np^2 mask bytes + the subtree ends)."""
+    metas = [pst.tree_meta_create(forest, t, stream) for t in range(len(sizes))]
+    npmax = max(s["n_padded"] for s in sizes)
+    buf = torch.empty(npmax * npmax, dtype=torch.uint8, device="cuda")
+    outs = [buf[:s["n_padded"] ** 2].view(s["n_padded"], s["n_padded"]) for s in sizes]
+
+    def one_pass():
+        for m, o in zip(metas, outs):
+            pst.tree_dense_mask(m, "u8", out=o, stream=stream)
+
+    one_pass()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / steps * 1e-3
+    for m in metas:
+        m.destroy()
+    del buf
+    return t, sum(s["n_padded"] ** 2 + 4 * s["n_padded"] for s in sizes)
 
 
 def host_packing(pst, w, forest, ranks=8, reps=5):

@@ -140,6 +140,18 @@ typedef struct {
 int pst_build_tree(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
                    int32_t max_tokens_per_mb, pst_forest** out);
 
+/* Build flags of pst_build_tree_ex. */
+enum { PST_BUILD_PAD_TO_MAXIMUM = 1 };
+
+/* pst_build_tree with flags.  PST_BUILD_PAD_TO_MAXIMUM pads every tree to
+ * max_tokens_per_mb rows instead of the next multiple of 128 (the
+ * pad_to_maximum setting of the tree-training page's configuration section:
+ * every micro-batch then has the same shape).  The extra rows are pad rows:
+ * token 0, position 0, parent -1, seeing only themselves.  Unknown flag bits:
+ * PST_EINVAL.  Other arguments and errors as pst_build_tree. */
+int pst_build_tree_ex(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
+                      int32_t max_tokens_per_mb, int32_t flags, pst_forest** out);
+
 int pst_forest_num_trees(const pst_forest* forest, int32_t* n_trees);
 int pst_forest_tree_sizes(const pst_forest* forest, int32_t tree, pst_tree_sizes* out);
 /* Copy tree `tree`'s arrays into the caller's host buffers (see pst_tree_arrays). */
@@ -261,6 +273,25 @@ int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int3
  * Errors: PST_EINVAL, PST_EDTYPE, PST_ESHAPE, PST_EHIP. */
 int pst_tree_rope(void* x, const pst_tree_meta* meta, int32_t n_heads, int32_t head_dim,
                   int32_t dtype, float theta, int32_t inverse, void* stream);
+
+/* ---- device: dense mask export ------------------------------------------ */
+
+/* Mask formats of pst_tree_dense_mask. */
+enum { PST_MASK_U8 = 0, PST_MASK_ADD_F32 = 1, PST_MASK_ADD_BF16 = 2 };
+
+/* Write the dense attention mask of the packed tree(s) behind `meta`, the
+ * tensor form that the tree-training page's Megatron section uses instead of
+ * a block mask so that it can be saved for gradient checkpointing.
+ *   out  device [Np, Np], row = query i, column = key j, 16-byte aligned,
+ *        Np = the metadata's padded rows (a forest's metadata gives its
+ *        block-diagonal mask); caller-owned, fully overwritten.
+ * Key j is visible to query i iff j is i or an ancestor of i (j <= i <=
+ * subtree_end[j] in preorder); pad rows see only themselves.
+ *   format  PST_MASK_U8: uint8, 1 visible, 0 hidden;
+ *           PST_MASK_ADD_F32 / PST_MASK_ADD_BF16: additive, 0 visible, -inf hidden.
+ * Errors: PST_EINVAL, PST_EDTYPE (unknown format), PST_ESHAPE (Np above
+ * 2 097 120 or misaligned out), PST_EHIP. */
+int pst_tree_dense_mask(const pst_tree_meta* meta, int32_t format, void* out, void* stream);
 
 /* ---- host: micro-batch / rank allocation -------------------------------- */
 

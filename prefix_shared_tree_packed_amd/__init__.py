@@ -22,4 +22,6 @@ from .api import (  # noqa: F401
     pack_allocate,
     packing_metrics,
     assign_trees,
+    MASK_FORMATS,
+    tree_dense_mask,
 )

@@ -53,6 +53,8 @@ class Stats(ctypes.Structure):
 
 
 PST_PACK_FFD, PST_PACK_KK = 0, 1
+PST_BUILD_PAD_TO_MAXIMUM = 1
+PST_MASK_U8, PST_MASK_ADD_F32, PST_MASK_ADD_BF16 = 0, 1, 2
 
 
 class PackMetrics(ctypes.Structure):
@@ -93,6 +95,8 @@ _SIGS = {
                                     P32]),
     "pst_pack_metrics_compute": (c_int32, [P64, c_int32, P32, c_int32, c_int64,
                                            POINTER(PackMetrics)]),
+    "pst_build_tree_ex": (c_int32, [P32, P64, c_int32, c_int32, c_int32, POINTER(c_void_p)]),
+    "pst_tree_dense_mask": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
     "pst_last_error": (c_char_p, []),
 }
 

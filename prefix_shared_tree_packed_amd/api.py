@@ -8,6 +8,7 @@ every computation happens in the library.  Names follow the C ABI:
     gather_tree_logprobs_entropy(logits, meta, ...) -> (logprobs, entropy)
     gather_tree_logprobs_entropy_bwd(logits, meta, dlogprobs, dentropy) -> dlogits
     tree_rope(x, meta, theta=None, inverse=False)  -> x rotated in place
+    tree_dense_mask(meta, format="u8")             -> [Np, Np] mask
     pack_allocate(values, capacity, ...)           -> (groups, fell_back)   (host)
     packing_metrics(values, groups, capacity)      -> dict                  (host)
     assign_trees(forest, n_ranks, ...)             -> rank of every tree    (host)
@@ -52,7 +53,7 @@ def _dev_tensor(t, name):
 class Forest:
     """Sequences packed into compressed tries (host, library-owned)."""
 
-    def __init__(self, seqs: Sequence, max_tokens_per_mb: int):
+    def __init__(self, seqs: Sequence, max_tokens_per_mb: int, pad_to_maximum: bool = False):
         lib = _lib.load()
         arrs = [np.ascontiguousarray(s, dtype=np.int32).ravel() for s in seqs]
         lens = np.array([a.size for a in arrs], dtype=np.int64)
@@ -62,9 +63,10 @@ class Forest:
         self.n_seqs = len(arrs)
         h = c_void_p()
         self._h = None
-        check(lib.pst_build_tree(
+        flags = _lib.PST_BUILD_PAD_TO_MAXIMUM if pad_to_maximum else 0
+        check(lib.pst_build_tree_ex(
             self._tokens.ctypes.data_as(_lib.P32), self._offsets.ctypes.data_as(_lib.P64),
-            int(self.n_seqs), int(max_tokens_per_mb), byref(h)))
+            int(self.n_seqs), int(max_tokens_per_mb), flags, byref(h)))
         self._h = h
         n = c_int32()
         check(lib.pst_forest_num_trees(self._h, byref(n)))
@@ -120,8 +122,10 @@ class Forest:
         return out
 
 
-def build_tree(seqs: Sequence, max_tokens_per_mb: int) -> Forest:
-    return Forest(seqs, max_tokens_per_mb)
+def build_tree(seqs: Sequence, max_tokens_per_mb: int, pad_to_maximum: bool = False) -> Forest:
+    """Pack sequences into compressed tries; pad_to_maximum pads every tree to
+    max_tokens_per_mb rows (fixed micro-batch shape)."""
+    return Forest(seqs, max_tokens_per_mb, pad_to_maximum)
 
 
 class TreeMeta:
@@ -332,3 +336,26 @@ def assign_trees(forest: Forest, n_ranks: int, cost: str = "pairs", algorithm: s
     for g, items in enumerate(groups):
         rank[items] = g
     return rank
+
+
+MASK_FORMATS = {"u8": _lib.PST_MASK_U8, "add_f32": _lib.PST_MASK_ADD_F32,
+                "add_bf16": _lib.PST_MASK_ADD_BF16}
+
+
+def tree_dense_mask(meta: TreeMeta, format: str = "u8", out=None, stream=None):
+    """Dense [Np, Np] attention mask of the tree(s) behind `meta` (row = query,
+    column = key): "u8" (1 visible), "add_f32" / "add_bf16" (0 visible, -inf
+    hidden).  Returns `out` (allocated when None)."""
+    import torch
+    if format not in MASK_FORMATS:
+        raise ValueError(f"unknown mask format {format!r}; valid: {sorted(MASK_FORMATS)}")
+    dt = {"u8": torch.uint8, "add_f32": torch.float32, "add_bf16": torch.bfloat16}[format]
+    Np = meta.n_padded
+    if out is None:
+        out = torch.empty((Np, Np), dtype=dt, device="cuda")
+    _dev_tensor(out, "out")
+    if out.dtype != dt or tuple(out.shape) != (Np, Np):
+        raise ValueError(f"out must be {dt} [{Np}, {Np}]")
+    check(_lib.load().pst_tree_dense_mask(meta._h, MASK_FORMATS[format],
+                                          c_void_p(out.data_ptr()), c_void_p(_stream_ptr(stream))))
+    return out

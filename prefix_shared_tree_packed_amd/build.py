@@ -40,6 +40,7 @@ HIP_SOURCES = [
     "kernels/attn_bwd_bf16.hip",
     "kernels/gather.hip",
     "kernels/rope.hip",
+    "kernels/mask.hip",
 ]
 CXX_SOURCES = ["host/forest.cpp", "host/packing.cpp"]
 

@@ -322,10 +322,12 @@ int pst_pack_metrics_compute(const int64_t* values, int32_t n, const int32_t* gr
 
 const char* pst_last_error(void) { return g_error.c_str(); }
 
-int pst_build_tree(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
-                   int32_t max_tokens_per_mb, pst_forest** out) {
+int pst_build_tree_ex(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
+                      int32_t max_tokens_per_mb, int32_t flags, pst_forest** out) {
   if (!out) return fail(PST_EINVAL, "out is NULL");
   *out = nullptr;
+  if (flags & ~PST_BUILD_PAD_TO_MAXIMUM)
+    return fail(PST_EINVAL, "unknown build flags " + std::to_string(flags));
   if (!seq_offsets) return fail(PST_EINVAL, "seq_offsets is NULL");
   if (n_seqs >= 1 && !tokens) return fail(PST_EINVAL, "tokens is NULL");
   pst_forest* f = new (std::nothrow) pst_forest;
@@ -333,7 +335,8 @@ int pst_build_tree(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_
   std::string err;
   int st;
   try {
-    st = pst::build_forest(tokens, seq_offsets, n_seqs, max_tokens_per_mb, f->f, err);
+    st = pst::build_forest(tokens, seq_offsets, n_seqs, max_tokens_per_mb,
+                           (flags & PST_BUILD_PAD_TO_MAXIMUM) != 0, f->f, err);
   } catch (const std::bad_alloc&) {
     delete f;
     return fail(PST_ENOMEM, "out of host memory while packing");
@@ -347,6 +350,11 @@ int pst_build_tree(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_
   }
   *out = f;
   return ok();
+}
+
+int pst_build_tree(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
+                   int32_t max_tokens_per_mb, pst_forest** out) {
+  return pst_build_tree_ex(tokens, seq_offsets, n_seqs, max_tokens_per_mb, 0, out);
 }
 
 int pst_forest_num_trees(const pst_forest* forest, int32_t* n_trees) {
@@ -563,6 +571,23 @@ int pst_tree_rope(void* x, const pst_tree_meta* meta, int32_t n_heads, int32_t h
                                         theta > 0.f ? theta : 10000.f, inverse != 0,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rope launch");
+  return ok();
+}
+
+int pst_tree_dense_mask(const pst_tree_meta* meta, int32_t format, void* out, void* stream) {
+  if (!meta) return fail(PST_EINVAL, "tree metadata is NULL");
+  if (format != PST_MASK_U8 && format != PST_MASK_ADD_F32 && format != PST_MASK_ADD_BF16)
+    return fail(PST_EDTYPE, "unknown mask format " + std::to_string(format));
+  if (meta->dev.Np / 32 > 65535)
+    return fail(PST_ESHAPE, "Np=" + std::to_string(meta->dev.Np) + " beyond the dense-mask limit");
+  if (int e = check_ptrs({out}, "out")) return e;
+  if (int e = check_meta_device(meta)) return e;
+  static_assert(PST_MASK_U8 == pst::kMaskU8 && PST_MASK_ADD_F32 == pst::kMaskAddF32 &&
+                    PST_MASK_ADD_BF16 == pst::kMaskAddBf16,
+                "mask format codes");
+  const hipError_t e =
+      pst::launch_dense_mask(format, meta->dev, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dense mask launch");
   return ok();
 }
 

@@ -87,9 +87,9 @@ struct Trie {
 };
 
 void flatten(const Trie& trie, int32_t tid, const int32_t* tokens, const int64_t* offsets,
-             const std::vector<int32_t>& path, Tree& t) {
+             const std::vector<int32_t>& path, int32_t pad_to, Tree& t) {
   const int32_t N = static_cast<int32_t>(trie.count);
-  const int32_t Np = (N + kBlock - 1) / kBlock * kBlock;
+  const int32_t Np = pad_to > 0 ? pad_to : (N + kBlock - 1) / kBlock * kBlock;
   const int32_t nb = Np / kBlock;
   t.id = tid;
   t.N = N;
@@ -301,7 +301,7 @@ void flatten(const Trie& trie, int32_t tid, const int32_t* tokens, const int64_t
 }  // namespace
 
 int build_forest(const int32_t* tokens, const int64_t* offsets, int32_t n_seqs,
-                 int32_t capacity, Forest& out, std::string& err) {
+                 int32_t capacity, bool pad_to_maximum, Forest& out, std::string& err) {
   if (capacity <= 0) {
     err = "max_tokens_per_mb must be positive, got " + std::to_string(capacity);
     return kBuildInvalid;
@@ -377,7 +377,8 @@ int build_forest(const int32_t* tokens, const int64_t* offsets, int32_t n_seqs,
 
   out.trees.resize(tries.size());
   for (size_t t = 0; t < tries.size(); ++t)
-    flatten(tries[t], static_cast<int32_t>(t), tokens, offsets, path, out.trees[t]);
+    flatten(tries[t], static_cast<int32_t>(t), tokens, offsets, path,
+            pad_to_maximum ? capacity : 0, out.trees[t]);
   return kBuildOk;
 }
 

@@ -19,7 +19,7 @@ constexpr int32_t kBlock = 128;
 struct Tree {
   int32_t id = 0;
   int32_t N = 0;    // real tree tokens
-  int32_t Np = 0;   // N rounded up to a multiple of kBlock
+  int32_t Np = 0;   // N rounded up to a multiple of kBlock (or the capacity)
   int32_t nb = 0;   // Np / kBlock
 
   // per flat token [Np]
@@ -62,9 +62,10 @@ struct Forest {
 
 enum BuildStatus { kBuildOk = 0, kBuildInvalid = -1, kBuildCapacity = -2, kBuildBlock = -3 };
 
-// Packs the sequences tokens[offsets[s] .. offsets[s+1]) into `out`.
-// Returns a BuildStatus; on failure `err` says why.
+// Packs the sequences tokens[offsets[s] .. offsets[s+1]) into `out`.  Trees
+// are padded to the next multiple of kBlock, or to `capacity` itself with
+// pad_to_maximum.  Returns a BuildStatus; on failure `err` says why.
 int build_forest(const int32_t* tokens, const int64_t* offsets, int32_t n_seqs,
-                 int32_t capacity, Forest& out, std::string& err);
+                 int32_t capacity, bool pad_to_maximum, Forest& out, std::string& err);
 
 }  // namespace pst

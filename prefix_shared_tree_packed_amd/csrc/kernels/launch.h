@@ -52,4 +52,9 @@ hipError_t launch_gather_bwd(int dtype, const void* logits, int64_t vocab, const
 hipError_t launch_rope(int dtype, void* x, const TreeDev& tr, int heads, int head_dim,
                        float theta, bool inverse, hipStream_t stream);
 
+// Dense [Np, Np] attention mask (row = query, column = key) in one of the
+// formats below; out is 16-byte aligned.
+enum { kMaskU8 = 0, kMaskAddF32 = 1, kMaskAddBf16 = 2 };
+hipError_t launch_dense_mask(int format, const TreeDev& tr, void* out, hipStream_t stream);
+
 }  // namespace pst

@@ -82,10 +82,10 @@ def attn_inputs(Np, hq, hkv, d, dtype, seed, device="cuda", with_dout=False):
 class Case:
     """One forest built twice: by the library (device metadata) and by the oracle."""
 
-    def __init__(self, seqs, cap):
+    def __init__(self, seqs, cap, pad_to_maximum=False):
         self.seqs = seqs
-        self.forest = pst.build_tree(seqs, cap)
-        self.ref = oracle.build_forest(seqs, cap)
+        self.forest = pst.build_tree(seqs, cap, pad_to_maximum=pad_to_maximum)
+        self.ref = oracle.build_forest(seqs, cap, pad_to_maximum=pad_to_maximum)
         assert self.forest.n_trees == len(self.ref.trees)
         self.metas = [pst.tree_meta_create(self.forest, t) for t in range(self.forest.n_trees)]
 

@@ -16,9 +16,9 @@ from workloads import WORKLOADS, get_workload, worked_example, worked_example_ed
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def compare_forest(seqs, cap):
-    ref = oracle.build_forest(seqs, cap)
-    got = pst.build_tree(seqs, cap)
+def compare_forest(seqs, cap, pad_to_maximum=False):
+    ref = oracle.build_forest(seqs, cap, pad_to_maximum=pad_to_maximum)
+    got = pst.build_tree(seqs, cap, pad_to_maximum=pad_to_maximum)
     assert got.n_trees == len(ref.trees)
     assert got.seq_tree().tolist() == ref.seq_tree.tolist()
     for t, rt in enumerate(ref.trees):
@@ -75,6 +75,18 @@ def test_brute_force_random():
         cap = int(rng.choice([128, 256])) if scale > 1 else 128
         seqs = [s[:cap] for s in seqs]
         compare_forest(seqs, cap)
+
+
+def test_pad_to_maximum():
+    rng = np.random.default_rng(12)
+    for trial in range(40):
+        n = int(rng.integers(1, 8))
+        seqs = [np.repeat(rng.integers(0, 4, size=int(rng.integers(1, 7))), 30).astype(np.int32)
+                for _ in range(n)]
+        cap = int(rng.choice([128, 256, 384]))
+        compare_forest([s[:cap] for s in seqs], cap, pad_to_maximum=True)
+    w = get_workload("grpo")
+    compare_forest(w.seqs, w.max_tokens_per_mb, pad_to_maximum=True)
 
 
 def test_wide_nodes():

@@ -33,6 +33,19 @@ def test_device_entry_points_reject_null_meta():
     assert _lib.ERRORS[rc] == "PST_EINVAL"
     rc = lib.pst_tree_rope(p, None, 8, 128, 1, 0.0, 0, None)
     assert _lib.ERRORS[rc] == "PST_EINVAL"
+    rc = lib.pst_tree_dense_mask(None, 0, p, None)
+    assert _lib.ERRORS[rc] == "PST_EINVAL"
+
+
+def test_build_rejects_unknown_flags():
+    import numpy as np
+    lib = pst.load()
+    toks = np.array([1, 2, 3], dtype=np.int32)
+    offs = np.array([0, 3], dtype=np.int64)
+    h = ctypes.c_void_p(1)
+    rc = lib.pst_build_tree_ex(toks.ctypes.data_as(_lib.P32), offs.ctypes.data_as(_lib.P64), 1,
+                               128, 2, ctypes.byref(h))
+    assert _lib.ERRORS[rc] == "PST_EINVAL" and not h.value
 
 
 def test_meta_create_rejects_bad_tree_index():
