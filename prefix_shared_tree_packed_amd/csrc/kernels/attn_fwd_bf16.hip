@@ -1,29 +1,37 @@
 // Tree attention forward pass, bf16 with head_dim 128: the performance path
 // on gfx950.  Same mathematics and work decomposition as attn_fwd.hip (one
-// workgroup per 128-row query block and query head, four waves of 32 rows,
-// S^T = K.Q^T with the query in the lane, O^T += V^T.P^T fed from the score
-// accumulators); what changes is how every step is fed:
+// workgroup per 128-row query block and query head, four waves of 32 rows);
+// what changes is how every step is fed:
 //
+//  * All products use v_mfma_f32_16x16x32_bf16.  A wave's 32 queries x 32
+//    keys of scores are four 16x16 blocks, accumulated as four independent
+//    chains over the four 32-deep slices of the head dimension (a dependent
+//    MFMA waits for its predecessor's result, so one chain alone would run
+//    at a fraction of the matrix core's rate), and O^T is sixteen
+//    independent 16x16 blocks.  S^T = K.Q^T puts one query in each lane
+//    column: a lane holds four keys of each block, so a query's row
+//    reductions span the four 16-lane groups (two permlane swaps).
 //  * Each non-empty 128x128 tile is walked in four 32-key steps through a
-//    double-buffered LDS pipeline: while the waves compute one step, the next
-//    step's K and V rows stream global -> LDS directly (global_load_lds_dwordx4:
-//    no VGPRs, no VALU) into row-major tiles (swizzle of lds_tiles.h).  One
-//    barrier per step.  33 KB of LDS and 168 VGPRs let three workgroups share
-//    a CU (three waves per SIMD), which measured faster than 64-key steps at
-//    two workgroups per CU: the kernel is bound by latency, not by LDS or
-//    HBM bandwidth.
+//    three-stage LDS ring: while the waves compute one step, the K and V rows
+//    and subtree ends of the step after next stream global -> LDS directly
+//    (global_load_lds_dwordx4: no VGPRs, no VALU) into row-major tiles
+//    (swizzle of lds_tiles.h); one barrier per step.  Two steps of lead
+//    hide the load latency under full traffic, which one step did not.
+//    48 KB of LDS and at most 168 VGPRs let three workgroups share a CU.
 //  * K rows are the A operand of S^T = K.Q^T as they stand (one 16-byte read
-//    per MFMA operand); the V^T operands of O^T += V^T.P^T come from the same
-//    row-major V tile through two ds_read_b64_tr_b16 transposing reads, whose
-//    slot order is the order in which the score accumulators feed P^T.
+//    per operand, shared by the two 16-query halves); the V^T operands of
+//    O^T += V^T.P^T come from the same row-major V tile through two
+//    ds_read_b64_tr_b16 transposing reads, whose key order is the order in
+//    which the score registers feed P^T.
 //  * The mask is evaluated per (wave, 32-key block): a block whose keys no
 //    query of the wave sees is skipped (no MFMA, no exp), a block every query
 //    sees runs unmasked, and only the rest pay the per-element test
 //    (unsigned)(i - j) <= se[j] - j, three VALU ops.
 //  * Scores stay unscaled; the softmax scale is folded into the exponent's
-//    FMA, and the running max is refreshed lazily: O and the row sum are
+//    FMA, and the running max is refreshed lazily: O and the row sums are
 //    rescaled only when a row's max grows by more than 2^8, so exponentials
-//    stay below 256 and most steps skip the rescale.
+//    stay below 256 and most steps skip the rescale.  Row sums stay per lane
+//    (each lane's own keys) until the end.
 #include "launch.h"
 #include "lds_tiles.h"
 #include "mfma.h"
@@ -36,32 +44,63 @@ namespace {
 constexpr int D = 128;
 constexpr int kStep = 32;              // keys per pipeline step
 constexpr int kSpt = kTile / kStep;    // steps per tile
-constexpr int kNkb = kStep / 32;       // 32-key blocks per step
 constexpr int kKRow = D * 2;              // K row: 256 B
 constexpr int kBufBytes = kStep * kKRow;  // 8 KB for K, 8 KB for V
+constexpr int kHalfTile = 16 * kKRow;     // byte offset of keys 16..31 of a step tile
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
 
 typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only: scalar loads
 
 __device__ __forceinline__ cint32* cst(const int32_t* p) { return (cint32*)(p); }
 
+__device__ __forceinline__ f32x4_t mma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int byte_off) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + byte_off));
+}
+
+// Max / sum over the four lanes l % 16 + 16 g (g = 0..3) that hold one query.
+__device__ __forceinline__ float quad_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  return max_halves(y);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  return sum_halves(y);
+}
+
+// V^T operand of one 16-row d block from a row-major V step tile: lane
+// (group g, index i) gets d = 16 db + i of keys 4g .. 4g+3 (slots 0..3) and
+// 16 + 4g .. 16 + 4g + 3 (slots 4..7), the key order of the score registers.
+// `trv` is the lane's byte offset for db = 0 (d blocks differ in bits 5..7).
+__device__ __forceinline__ bf16x8_t lds_vt_frag(const uint8_t* tile, int trv, int db) {
+  const int off = trv ^ (db << 5);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + kHalfTile + off));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, w);
 }
 
 __global__ __launch_bounds__(256, 3) void tree_attn_fwd_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ o, float* __restrict__ lse, TreeDev tr, int hq, int hkv, float c) {
-  using M = Mfma<bf16_t>;
   // two separately named buffers (not one array indexed by the step parity)
   // so the compiler can tell the in-flight DMA target from the buffer being
   // read and does not drain the prefetch before every LDS read
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[kBufBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t vt_lds0[kBufBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t vt_lds1[kBufBytes];
-  __shared__ __attribute__((aligned(16))) int32_t span_lds0[kStep];
-  __shared__ __attribute__((aligned(16))) int32_t span_lds1[kStep];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[kBufBytes];
+  __shared__ __attribute__((aligned(16))) int32_t se_lds0[kStep];
+  __shared__ __attribute__((aligned(16))) int32_t se_lds1[kStep];
+  __shared__ __attribute__((aligned(16))) int32_t se_lds2[kStep];
 
   const int G = hq / hkv;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -76,33 +115,40 @@ __global__ __launch_bounds__(256, 3) void tree_attn_fwd_bf16_d128(
   // wave index as a scalar, so the per-wave block classes branch on SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const int lq = lane % 32;
-  const int half = lane / 32;
+  const int li = lane % 16;  // query column of the 16x16 blocks
+  const int lg = lane / 16;  // 16-lane group: keys 4 lg .. 4 lg + 3 of each block
   const int qlo = qb * kTile + wave * 32;  // first query row of this wave
-  const int qrow = qlo + lq;
 
-  bf16x8_t qf[8];
-  {
-    const bf16_t* qp = q + (static_cast<size_t>(qrow) * hq + h) * D + half * 8;
+  // B operands of S^T = K.Q^T: query qlo + 16 qh + li, d = 32 s + 8 lg .. +7
+  bf16x8_t qf[2][4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = M::load(qp + 16 * s);
+  for (int qh = 0; qh < 2; ++qh) {
+    const bf16_t* qp = q + (static_cast<size_t>(qlo + 16 * qh + li) * hq + h) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[qh][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 32 * s));
   }
-  // LDS byte offsets of this lane's 16-byte K chunk for contraction step s
-  // (row lq of a 32-key block); V^T operands come through transposing reads
-  int koff_rd[8];
+  // A operands: key row li (+16 for the second key half), chunk 4 s + lg
+  int koff[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) koff_rd[s] = lq * kKRow + (((2 * s + half) ^ rsw(lq)) << 4);
-  const TrOff tro = tr_offsets(lane);
+  for (int s = 0; s < 4; ++s) koff[s] = li * kKRow + (((4 * s + lg) ^ rsw(li)) << 4);
+  // V^T reads: lane i of group lg addresses key 4 lg + i / 4 at d = 4 (i % 4) .. +3
+  int trv;
+  {
+    const int t = 4 * lg + li / 4;
+    const int a = li % 4;
+    trv = t * kKRow + ((((a >> 1) ^ rsw(t))) << 4) + ((a & 1) << 3);
+  }
 
   // Global loads: a wave-uniform base pointer plus a 32-bit lane offset.
   const uint32_t kv_bytes = static_cast<uint32_t>(hkv) * D * 2;  // one token's K (or V) rows
   const char* kgb = reinterpret_cast<const char*>(k + static_cast<size_t>(g) * D);
   const char* vgb = reinterpret_cast<const char*>(v + static_cast<size_t>(g) * D);
 
-  f32x16_t oacc[4];
+  f32x4_t oacc[8][2];  // O^T block (d block db, query half qh)
 #pragma unroll
-  for (int b = 0; b < 4; ++b) oacc[b] = f32x16_t{};
-  float m_used = -INFINITY, l = 0.f;
+  for (int db = 0; db < 8; ++db) oacc[db][0] = oacc[db][1] = f32x4_t{};
+  float m_used[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};  // this lane's share of each row sum
 
   cint32* q_ptr = cst(tr.q_ptr);
   cint32* q_tile = cst(tr.q_tile);
@@ -113,145 +159,140 @@ __global__ __launch_bounds__(256, 3) void tree_attn_fwd_bf16_d128(
   auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + st / kSpt); };
   auto step_key0 = [&](int st) { return (q_tile[tile_of(st)] >> 1) * kTile + kStep * (st % kSpt); };
 
-  int4 se4 = make_int4(0, 0, 0, 0);
-  auto issue_loads = [&](int st, uint8_t* kdst, uint8_t* vdst) {
+  // Staging of one step: the subtree ends of its keys (eight lanes of wave
+  // 0) and its K and V rows, all global -> LDS.  Every wave issues kDmaOps
+  // DMA instructions per step (wave 0 one more, first), so a wait for
+  // vmcnt(kDmaOps) lands every step but the newest.
+  constexpr int kDmaOps = 2 * (kStep / 16);
+  auto issue_loads = [&](int st, uint8_t* kdst, uint8_t* vdst, int32_t* sdst) {
     const int k0 = step_key0(st);
-    // every lane loads (lanes past 16 repeat a quad; only 16 are stored), so
-    // no load sits in a divergent branch; first, so that its wait leaves the
-    // DMA in flight
-    se4 = *reinterpret_cast<const int4*>(tr.se + k0 + 4 * (tid & 15));
+    if (wave == 0 && lane < kStep / 4)
+      __builtin_amdgcn_global_load_lds(tr.se + k0 + 4 * lane, (lds_void*)sdst, 16, 0, 0);
     dma_tile<kStep>(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kdst, wave, lane);
     dma_tile<kStep>(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vdst, wave, lane);
   };
-  auto store_span = [&](int st, int32_t* sdst) {
-    if (tid < kStep / 4) {
-      const int key = step_key0(st) + 4 * tid;
-      const int4 span = make_int4(se4.x - key, se4.y - key - 1, se4.z - key - 2, se4.w - key - 3);
-      *reinterpret_cast<int4*>(sdst + 4 * tid) = span;
-    }
-  };
 
   auto step = [&](int st, const uint8_t* kcur, const uint8_t* vcur, const int32_t* scur,
-                  uint8_t* knext, uint8_t* vnext, int32_t* snext) {
+                  uint8_t* kfill, uint8_t* vfill, int32_t* sfill) {
     const int k0 = step_key0(st);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // step st staged by every wave; step st-1 consumed
-    // prefetch the next step; after the last step this reloads the last step
-    // into the idle buffer (in bounds, never read) so the code stays
-    // branch-free and the compiler keeps the DMA and the reads apart
-    const int st_next = st + 1 < n_steps ? st + 1 : st;
-    issue_loads(st_next, knext, vnext);
+    // step st staged by every wave (each waits for its own DMA), step st-1's
+    // LDS reads returned; a plain s_barrier, since a workgroup fence would
+    // also drain the newer prefetch
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaOps) : "memory");
+    // prefetch two steps ahead into the buffer step st-1 used; past the end
+    // the last step again (in bounds, never read), so the code stays
+    // branch-free and the count of outstanding DMA stays fixed
+    issue_loads(st + 2 < n_steps ? st + 2 : n_steps - 1, kfill, vfill, sfill);
 
-    // class of this wave's two 32x32 sub-blocks: 0 empty, 1 partial, 2 full
-    const uint32_t bits = static_cast<uint32_t>(q_cls[tile_of(st)]);
-    int cls[kNkb];
+    // class of this wave's 32x32 block: 0 empty, 1 partial, 2 full
+    const uint32_t cls =
+        (static_cast<uint32_t>(q_cls[tile_of(st)]) >> (2 * (4 * wave + st % kSpt))) & 3;
+    if (cls) {
+      // S^T blocks (key half kh, query half qh): four independent chains
+      f32x4_t sacc[2][2];
 #pragma unroll
-    for (int kb = 0; kb < kNkb; ++kb) cls[kb] = (bits >> (2 * (4 * wave + kNkb * (st % kSpt) + kb))) & 3;
-
-    bool any_cls = false;
+      for (int kh = 0; kh < 2; ++kh) sacc[kh][0] = sacc[kh][1] = f32x4_t{};
 #pragma unroll
-    for (int kb = 0; kb < kNkb; ++kb) any_cls |= cls[kb] != 0;
-    if (any_cls) {
-      // S^T = K.Q^T for the non-empty 32-key blocks
-      f32x16_t sacc[kNkb];
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int kb = 0; kb < kNkb; ++kb) {
-        sacc[kb] = f32x16_t{};
-        if (cls[kb]) {
-#pragma unroll
-          for (int s = 0; s < 8; ++s)
-            sacc[kb] = M::mma(lds_frag(kcur, kb * 32 * kKRow + koff_rd[s]), qf[s], sacc[kb]);
+        for (int kh = 0; kh < 2; ++kh) {
+          const bf16x8_t kf = lds_frag(kcur, kh * kHalfTile + koff[s]);
+          sacc[kh][0] = mma16(kf, qf[0][s], sacc[kh][0]);
+          sacc[kh][1] = mma16(kf, qf[1][s], sacc[kh][1]);
         }
-      }
 
-      // mask partial blocks; row max of the raw scores
-      float mx = -INFINITY;
-      const int A = qrow - k0 - 4 * half;
+      // mask a partial block; row max of the raw scores (register i of block
+      // (kh, qh) is key 16 kh + 4 lg + i of query qlo + 16 qh + li)
+      float mx[2];
 #pragma unroll
-      for (int kb = 0; kb < kNkb; ++kb) {
-        if (cls[kb] == 1) {
+      for (int qh = 0; qh < 2; ++qh) {
+        float m = -INFINITY;
+        const int A = qlo + 16 * qh + li - k0 - 4 * lg;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int4 sp = *reinterpret_cast<const int4*>(scur + 32 * kb + 8 * i + 4 * half);
-            const int spv[4] = {sp.x, sp.y, sp.z, sp.w};
+        for (int kh = 0; kh < 2; ++kh) {
+          if (cls == 1) {
+            // key j sees query q iff (unsigned)(q - j) <= se[j] - j
+            const int4 sev = *reinterpret_cast<const int4*>(scur + 16 * kh + 4 * lg);
+            const int sea[4] = {sev.x, sev.y, sev.z, sev.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t dlt = static_cast<uint32_t>(A - (32 * kb + 8 * i + j));
-              const float x = dlt <= static_cast<uint32_t>(spv[j]) ? sacc[kb][4 * i + j] : -INFINITY;
-              sacc[kb][4 * i + j] = x;
-              mx = fmaxf(mx, x);
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t dlt = static_cast<uint32_t>(A - (16 * kh + i));
+              const int span = sea[i] - (k0 + 4 * lg + 16 * kh + i);
+              const float x = dlt <= static_cast<uint32_t>(span) ? sacc[kh][qh][i] : -INFINITY;
+              sacc[kh][qh][i] = x;
+              m = fmaxf(m, x);
             }
-          }
-        } else if (cls[kb] == 2) {
+          } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-        }
-      }
-      mx = max_halves(mx);
-      const float mxc = mx * c;
-      if (__any(mxc > m_used + kRescale)) {
-        const float m_new = fmaxf(m_used, mxc);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_used - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) oacc[b] *= alpha;
-        m_used = m_new;
-      }
-      const float negm = m_used == -INFINITY ? 0.f : -m_used;
-      float sum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < kNkb; ++kb) {
-        if (cls[kb]) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(sacc[kb][r], c, negm));
-            sacc[kb][r] = p;
-            sum += p;
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[kh][qh][i]);
           }
         }
+        mx[qh] = quad_max(m) * c;
       }
-      sum = sum_halves(sum);
-      l += sum;
+      if (__any(mx[0] > m_used[0] + kRescale || mx[1] > m_used[1] + kRescale)) {
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          const float m_new = fmaxf(m_used[qh], mx[qh]);
+          const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_used[qh] - m_new);
+          l_part[qh] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) oacc[db][qh] *= alpha;
+          m_used[qh] = m_new;
+        }
+      }
+      bf16x8_t pf[2];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        const float negm = m_used[qh] == -INFINITY ? 0.f : -m_used[qh];
+        float e[8];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[4 * kh + i] = fast_exp2(fmaf(sacc[kh][qh][i], c, negm));
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) s += e[r];
+        l_part[qh] += s;
+        typedef float f32x8_t __attribute__((ext_vector_type(8)));
+        const f32x8_t ev = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
+        pf[qh] = __builtin_convertvector(ev, bf16x8_t);
+      }
 
-      // O^T += V^T.P^T
+      // O^T += V^T.P^T: sixteen independent blocks
 #pragma unroll
-      for (int kb = 0; kb < kNkb; ++kb) {
-        if (cls[kb]) {
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8_t pf = M::from_acc(sacc[kb], s2);
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-              oacc[b] = M::mma(lds_tr_frag(vcur, tro, 32 * kb + 16 * s2, 32 * b), pf, oacc[b]);
-          }
-        }
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8_t vf = lds_vt_frag(vcur, trv, db);
+        oacc[db][0] = mma16(vf, pf[0], oacc[db][0]);
+        oacc[db][1] = mma16(vf, pf[1], oacc[db][1]);
       }
     }
-
-    store_span(st_next, snext);
   };
 
   if (n_steps > 0) {
-    issue_loads(0, k_lds0, vt_lds0);
-    store_span(0, span_lds0);
+    issue_loads(0, k_lds0, v_lds0, se_lds0);
+    issue_loads(1, k_lds1, v_lds1, se_lds1);  // n_steps >= 4
   }
-  for (int st = 0; st < n_steps; st += 2) {  // n_steps is a multiple of kSpt, so even
-    step(st, k_lds0, vt_lds0, span_lds0, k_lds1, vt_lds1, span_lds1);
-    step(st + 1, k_lds1, vt_lds1, span_lds1, k_lds0, vt_lds0, span_lds0);
+  for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses buffer st % 3
+    step(st, k_lds0, v_lds0, se_lds0, k_lds2, v_lds2, se_lds2);
+    if (st + 1 < n_steps) step(st + 1, k_lds1, v_lds1, se_lds1, k_lds0, v_lds0, se_lds0);
+    if (st + 2 < n_steps) step(st + 2, k_lds2, v_lds2, se_lds2, k_lds1, v_lds1, se_lds1);
   }
+  // the last steps' prefetch must land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const float inv = 1.f / l;
-  bf16_t* op = o + (static_cast<size_t>(qrow) * hq + h) * D;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int qh = 0; qh < 2; ++qh) {
+    const float l = quad_sum(l_part[qh]);
+    const float inv = 1.f / l;
+    const int qrow = qlo + 16 * qh + li;
+    bf16_t* op = o + (static_cast<size_t>(qrow) * hq + h) * D + 4 * lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = b * 32 + 8 * i + 4 * half;
-      store4<bf16_t>(op + d, oacc[b][4 * i] * inv, oacc[b][4 * i + 1] * inv,
-                     oacc[b][4 * i + 2] * inv, oacc[b][4 * i + 3] * inv);
-    }
-  if (half == 0)
-    lse[static_cast<size_t>(h) * tr.Np + qrow] = (m_used + fast_log2(l)) * 0.69314718055994531f;
+    for (int db = 0; db < 8; ++db)
+      store4<bf16_t>(op + 16 * db, oacc[db][qh][0] * inv, oacc[db][qh][1] * inv,
+                     oacc[db][qh][2] * inv, oacc[db][qh][3] * inv);
+    if (lg == 0)
+      lse[static_cast<size_t>(h) * tr.Np + qrow] = (m_used[qh] + fast_log2(l)) * 0.69314718055994531f;
+  }
 }
 
 }  // namespace
