@@ -5,9 +5,14 @@
 // list), fed the way the forward kernel of attn_fwd_bf16.hip is fed:
 //
 //  * Every tile reaches LDS row-major (token rows of 256 bytes) by
-//    global_load_lds_dwordx4 (no VGPRs, no VALU), double-buffered through
-//    two named buffers: Q and dO in 64-query steps for dK/dV (one workgroup
-//    per CU), K and V in 32-key steps for dQ (two workgroups per CU).
+//    global_load_lds_dwordx4 (no VGPRs, no VALU): Q and dO in 64-query steps
+//    through a three-stage ring for dK/dV (one workgroup per CU; the DMA is
+//    issued from inline assembly so that only the kernel's own waits gate
+//    it), K and V in 32-key steps double-buffered for dQ (two workgroups per
+//    CU).
+//  * dK/dV uses 16x16x32 MFMAs throughout, so its one wave per SIMD always
+//    has eight independent score chains and sixteen independent dK / dV
+//    blocks in flight; dQ keeps 32x32x16 tiles.
 //  * Products that contract over tokens need the tile transposed (dV^T +=
 //    dO^T.P, dK^T += Q^T.dS, dQ^T += K^T.dS^T).  Their A operands come from
 //    the same row-major tile through ds_read_b64_tr_b16: two transposing
@@ -72,23 +77,50 @@ __global__ __launch_bounds__(256) void bwd_dsum_bf16(const bf16_t* __restrict__ 
 }
 
 // --------------------------------------------------------------------- dK, dV
+// A wave owns 32 keys (two 16-key halves kh) of one key/value head and walks
+// every visible query block of the G query heads in 64-query steps (three
+// stages of LDS, one workgroup per CU).  All products are 16x16x32 MFMAs:
+// per 32-query slice, S = Q.K^T and dP = dO.V^T are eight independent
+// 16x16 chains, and dV^T += dO^T.P, dK^T += Q^T.dS sixteen independent
+// blocks each, so one wave per SIMD keeps the matrix core busy.
 constexpr int kKvStep = 64;                 // queries per step
 constexpr int kKvBuf = kKvStep * kRowB;     // 16 KB
+constexpr int kHalf16 = 16 * kRowB;         // byte offset of rows 16..31 of a 32-row slice
+// stage layout: Q tile | dO tile | LSE [64] | D [64]
+constexpr int kStDo = kKvBuf, kStLs = 2 * kKvBuf, kStDd = 2 * kKvBuf + 4 * kKvStep;
+constexpr int kStageB = 2 * kKvBuf + 8 * kKvStep;
+
+__device__ __forceinline__ f32x4_t mma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Transposed operand of one 16-row d block from a row-major 32-token slice:
+// lane (group g, index i) gets d = 16 db + i of tokens 4g .. 4g+3 (slots
+// 0..3) and 16 + 4g .. 16 + 4g + 3 (slots 4..7), the token order in which
+// 16x16 accumulators feed a B operand.
+__device__ __forceinline__ bf16x8_t lds_t16_frag(const uint8_t* slice, int trv, int db) {
+  const int off = trv ^ (db << 5);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(slice + off));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(slice + kHalf16 + off));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+__device__ __forceinline__ bf16x8_t pack8(const f32x4_t& lo, const f32x4_t& hi) {
+  typedef float f32x8_t __attribute__((ext_vector_type(8)));
+  const f32x8_t x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_convertvector(x, bf16x8_t);
+}
 
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, TreeDev tr, int hq, int hkv, float c,
     float scale) {
-  using M = Mfma<bf16_t>;
-  __shared__ __attribute__((aligned(1024))) uint8_t q_l0[kKvBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t q_l1[kKvBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t do_l0[kKvBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t do_l1[kKvBuf];
-  __shared__ __attribute__((aligned(16))) float ls_l0[kKvStep];
-  __shared__ __attribute__((aligned(16))) float ls_l1[kKvStep];
-  __shared__ __attribute__((aligned(16))) float dd_l0[kKvStep];
-  __shared__ __attribute__((aligned(16))) float dd_l1[kKvStep];
+  // one named array per stage (Q tile, dO tile, LSE, D), so the compiler
+  // tells the in-flight DMA target from the stage being read
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageB];
 
   const int G = hq / hkv;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -98,34 +130,46 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const int lq = lane % 32;
-  const int half = lane / 32;
+  const int li = lane % 16;  // key column of the 16x16 blocks
+  const int lg = lane / 16;  // 16-lane group: queries 4 lg .. 4 lg + 3 of each block
   const int kbase = kb * kTile + 32 * wave;  // first key of this wave
-  const int key = kbase + lq;
-  const int span_k = tr.se[key] - key;
+  int span_k[2];             // se - key of this lane's key in each half
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) span_k[kh] = tr.se[kbase + 16 * kh + li] - (kbase + 16 * kh + li);
   cint32* blk32 = cst(tr.blk32);
   const int smin = blk32[2 * (kbase >> 5)], smax = blk32[2 * (kbase >> 5) + 1];
 
-  bf16x8_t kf[8], vf[8];
-  {
-    const size_t off = (static_cast<size_t>(key) * hkv + g) * D + half * 8;
+  // B operands K^T / V^T: key kbase + 16 kh + li, d = 32 s + 8 lg .. +7
+  bf16x8_t kf[2][4], vf[2][4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kf[s] = M::load(k + off + 16 * s);
-      vf[s] = M::load(v + off + 16 * s);
+  for (int kh = 0; kh < 2; ++kh) {
+    const size_t off = (static_cast<size_t>(kbase + 16 * kh + li) * hkv + g) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kf[kh][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(k + off + 32 * s));
+      vf[kh][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(v + off + 32 * s));
     }
   }
-  int roff[8];  // row operand: row lq of a 32-row block, contraction step s
+  // A operands Q / dO: query row li of a 16-row block, chunk 4 s + lg
+  int roff[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) roff[s] = lq * kRowB + (((2 * s + half) ^ rsw(lq)) << 4);
-  const TrOff tro = tr_offsets(lane);
-
-  f32x16_t dkacc[4], dvacc[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    dkacc[b] = f32x16_t{};
-    dvacc[b] = f32x16_t{};
+  for (int s = 0; s < 4; ++s) roff[s] = li * kRowB + (((4 * s + lg) ^ rsw(li)) << 4);
+  // transposed reads: lane i of group lg addresses token 4 lg + i / 4 at d = 4 (i % 4) .. +3
+  int trv;
+  {
+    const int t = 4 * lg + li / 4;
+    const int a = li % 4;
+    trv = t * kRowB + ((((a >> 1) ^ rsw(t))) << 4) + ((a & 1) << 3);
   }
+
+  f32x4_t dkacc[8][2], dvacc[8][2];  // (d block db, key half kh)
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      dkacc[db][kh] = f32x4_t{};
+      dvacc[db][kh] = f32x4_t{};
+    }
 
   const uint32_t q_bytes = static_cast<uint32_t>(hq) * D * 2;  // one token's Q (or dO) rows
   const int qhi = cst(tr.kb_qhi)[kb];
@@ -138,103 +182,138 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
     h = g * G + r;
     q0 = qb * kTile + kKvStep * (st & 1);
   };
-  auto issue_loads = [&](int st, uint8_t* ql, uint8_t* dol, float* lsl, float* ddl) {
+  // Every wave issues kDmaOps tile DMA instructions per step; waves 0 and 1
+  // also one for LSE / D, first, so a wait for vmcnt(kDmaOps) lands every
+  // step but the newest.
+  constexpr int kDmaOps = 2 * (kKvStep / 16);
+  auto issue_loads = [&](int st, uint8_t* stg) {
     int qb, h, q0;
     decode(st, qb, h, q0);
-    const size_t row0 = static_cast<size_t>(q0) * q_bytes + static_cast<size_t>(h) * D * 2;
-    dma_tile<kKvStep>(reinterpret_cast<const char*>(q) + row0, q_bytes, ql, wave, lane);
-    dma_tile<kKvStep>(reinterpret_cast<const char*>(dout) + row0, q_bytes, dol, wave, lane);
     const size_t r0 = static_cast<size_t>(h) * tr.Np + q0;
+    const uint32_t base = lds_addr(stg);
     if (wave == 0)
-      __builtin_amdgcn_global_load_lds(lse + r0 + lane, (lds_void*)lsl, 4, 0, 0);
+      dma4_asm(lse + r0 + lane, base + kStLs);
     else if (wave == 1)
-      __builtin_amdgcn_global_load_lds(dsum + r0 + lane, (lds_void*)ddl, 4, 0, 0);
+      dma4_asm(dsum + r0 + lane, base + kStDd);
+    const size_t row0 = static_cast<size_t>(q0) * q_bytes + static_cast<size_t>(h) * D * 2;
+    dma_tile_asm<kKvStep>(reinterpret_cast<const char*>(q) + row0, q_bytes, base, wave, lane);
+    dma_tile_asm<kKvStep>(reinterpret_cast<const char*>(dout) + row0, q_bytes, base + kStDo, wave, lane);
   };
 
-  auto step = [&](int st, const uint8_t* ql, const uint8_t* dol, const float* lsl, const float* ddl,
-                  uint8_t* nql, uint8_t* ndol, float* nlsl, float* nddl) {
+  auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
+    const uint8_t* ql = stg;
+    const uint8_t* dol = stg + kStDo;
+    const float* lsl = reinterpret_cast<const float*>(stg + kStLs);
+    const float* ddl = reinterpret_cast<const float*>(stg + kStDd);
     int qb, h, q0;
     decode(st, qb, h, q0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // step st staged; step st-1 consumed
-    const int st_next = st + 1 < n_steps ? st + 1 : st;
-    issue_loads(st_next, nql, ndol, nlsl, nddl);
+    // step st staged by every wave, step st-1's LDS reads returned; a plain
+    // s_barrier, since a workgroup fence would also drain the newer prefetch
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaOps) : "memory");
+    issue_loads(st + 2 < n_steps ? st + 2 : n_steps - 1, fill);
 
-    const int A = q0 + 4 * half - key;  // (query - key) of register 0 of sub-block 0
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int qlo = q0 + 32 * qs;
       const bool empty = kbase > qlo + 31 || smax < qlo;
       if (empty) continue;
       const bool full = kbase + 31 <= qlo && smin >= qlo + 31;
+      const uint8_t* qsl = ql + 32 * qs * kRowB;
+      const uint8_t* dosl = dol + 32 * qs * kRowB;
 
-      // S = Q.K^T: rows are queries, this lane's column is its key
-      f32x16_t p = f32x16_t{};
+      // S and dP blocks (query half q16, key half kh): eight chains
+      f32x4_t sacc[2][2], dpacc[2][2];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) p = M::mma(lds_frag(ql, qs * 32 * kRowB + roff[s]), kf[s], p);
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 l4 = *reinterpret_cast<const float4*>(lsl + 32 * qs + 8 * i + 4 * half);
-        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+        for (int b = 0; b < 2; ++b) sacc[a][b] = dpacc[a][b] = f32x4_t{};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = fast_exp2(fmaf(p[4 * i + j], c, -lv[j]));
-          if (full) {
-            p[4 * i + j] = e;
-          } else {
-            const uint32_t dlt = static_cast<uint32_t>(A + 32 * qs + 8 * i + j);
-            p[4 * i + j] = dlt <= static_cast<uint32_t>(span_k) ? e : 0.f;
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int q16 = 0; q16 < 2; ++q16) {
+          const bf16x8_t qa = lds_frag(qsl, q16 * kHalf16 + roff[s]);
+          const bf16x8_t da = lds_frag(dosl, q16 * kHalf16 + roff[s]);
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            sacc[q16][kh] = mma16(qa, kf[kh][s], sacc[q16][kh]);
+            dpacc[q16][kh] = mma16(da, vf[kh][s], dpacc[q16][kh]);
           }
         }
+      // P = exp(S c - LSE) on visible pairs (register i of block (q16, kh) is
+      // query qlo + 16 q16 + 4 lg + i, key kbase + 16 kh + li); dS = P (dP - D)
+#pragma unroll
+      for (int q16 = 0; q16 < 2; ++q16) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lsl + 32 * qs + 16 * q16 + 4 * lg);
+        const float4 d4 = *reinterpret_cast<const float4*>(ddl + 32 * qs + 16 * q16 + 4 * lg);
+        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float e = fast_exp2(fmaf(sacc[q16][kh][i], c, -lv[i]));
+            if (!full) {
+              const uint32_t dlt =
+                  static_cast<uint32_t>(qlo + 16 * q16 + 4 * lg + i - (kbase + 16 * kh + li));
+              e = dlt <= static_cast<uint32_t>(span_k[kh]) ? e : 0.f;
+            }
+            sacc[q16][kh][i] = e;
+            dpacc[q16][kh][i] = e * (dpacc[q16][kh][i] - dd[i]);
+          }
       }
-      // dV^T += dO^T.P
+      bf16x8_t pf[2], sf[2];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8_t pf = M::from_acc(p, s2);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          dvacc[b] = M::mma(lds_tr_frag(dol, tro, 32 * qs + 16 * s2, 32 * b), pf, dvacc[b]);
+      for (int kh = 0; kh < 2; ++kh) {
+        pf[kh] = pack8(sacc[0][kh], sacc[1][kh]);
+        sf[kh] = pack8(dpacc[0][kh], dpacc[1][kh]);
       }
-      // dP = dO.V^T, dS = P (dP - D)
-      f32x16_t dp = f32x16_t{};
+      // dV^T += dO^T.P, dK^T += Q^T.dS
 #pragma unroll
-      for (int s = 0; s < 8; ++s) dp = M::mma(lds_frag(dol, qs * 32 * kRowB + roff[s]), vf[s], dp);
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8_t dot = lds_t16_frag(dosl, trv, db);
+        const bf16x8_t qt = lds_t16_frag(qsl, trv, db);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 d4 = *reinterpret_cast<const float4*>(ddl + 32 * qs + 8 * i + 4 * half);
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[4 * i + j] *= dp[4 * i + j] - dv4[j];
-      }
-      // dK^T += Q^T.dS
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8_t sf = M::from_acc(p, s2);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          dkacc[b] = M::mma(lds_tr_frag(ql, tro, 32 * qs + 16 * s2, 32 * b), sf, dkacc[b]);
+        for (int kh = 0; kh < 2; ++kh) {
+          dvacc[db][kh] = mma16(dot, pf[kh], dvacc[db][kh]);
+          dkacc[db][kh] = mma16(qt, sf[kh], dkacc[db][kh]);
+        }
       }
     }
   };
 
-  if (n_steps > 0) issue_loads(0, q_l0, do_l0, ls_l0, dd_l0);
-  for (int st = 0; st < n_steps; st += 2) {  // n_steps is even
-    step(st, q_l0, do_l0, ls_l0, dd_l0, q_l1, do_l1, ls_l1, dd_l1);
-    step(st + 1, q_l1, do_l1, ls_l1, dd_l1, q_l0, do_l0, ls_l0, dd_l0);
+  // the K, V and subtree-end loads above complete here (empty asm uses pin
+  // them before the loop): the compiler's own waits for them would otherwise
+  // sit inside the loop and, not counting the assembly DMA, drain the
+  // prefetch
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    asm volatile("" ::"v"(span_k[kh]));
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) asm volatile("" ::"v"(kf[kh][s4]), "v"(vf[kh][s4]));
   }
+  if (n_steps > 0) {
+    issue_loads(0, stage0);
+    issue_loads(1, stage1);  // n_steps >= 2
+  }
+  for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses stage st % 3
+    step(st, stage0, stage2);
+    if (st + 1 < n_steps) step(st + 1, stage1, stage0);
+    if (st + 2 < n_steps) step(st + 2, stage2, stage1);
+  }
+  // the last steps' prefetch must land before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const size_t off = (static_cast<size_t>(key) * hkv + g) * D;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int kh = 0; kh < 2; ++kh) {
+    const size_t off = (static_cast<size_t>(kbase + 16 * kh + li) * hkv + g) * D + 4 * lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = b * 32 + 8 * i + 4 * half;
-      store4<bf16_t>(dk + off + d, dkacc[b][4 * i] * scale, dkacc[b][4 * i + 1] * scale,
-                     dkacc[b][4 * i + 2] * scale, dkacc[b][4 * i + 3] * scale);
-      store4<bf16_t>(dv + off + d, dvacc[b][4 * i], dvacc[b][4 * i + 1], dvacc[b][4 * i + 2],
-                     dvacc[b][4 * i + 3]);
+    for (int db = 0; db < 8; ++db) {
+      store4<bf16_t>(dk + off + 16 * db, dkacc[db][kh][0] * scale, dkacc[db][kh][1] * scale,
+                     dkacc[db][kh][2] * scale, dkacc[db][kh][3] * scale);
+      store4<bf16_t>(dv + off + 16 * db, dvacc[db][kh][0], dvacc[db][kh][1], dvacc[db][kh][2],
+                     dvacc[db][kh][3]);
     }
+  }
 }
 
 // --------------------------------------------------------------------- dQ

@@ -37,6 +37,40 @@ __device__ __forceinline__ void dma_tile(const char* src, uint32_t stride, uint8
   }
 }
 
+// Same staging as dma_tile, issued through inline assembly (M0 = LDS base),
+// so the compiler does not track it as an LDS store: it then inserts no
+// conservative vmcnt(0) before reads of other buffers, and the caller owns
+// every wait (vmcnt) and the barrier (whose "memory" clobber orders the LDS
+// reads after it).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) uint8_t*)(p)));
+}
+__device__ __forceinline__ void dma16_asm(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(src)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_asm(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_base), "v"(src)
+               : "memory", "m0");
+}
+template <int NROWS>
+__device__ __forceinline__ void dma_tile_asm(const char* src, uint32_t stride, uint32_t dst, int wave,
+                                             int lane) {
+#pragma unroll
+  for (int i = 0; i < NROWS / 16; ++i) {
+    const int n = (NROWS / 16) * wave + i;
+    const int r = 4 * n + (lane >> 4);
+    const int cch = (lane & 15) ^ rsw(r);
+    dma16_asm(src + static_cast<size_t>(r) * stride + (cch << 4),
+              __builtin_amdgcn_readfirstlane(dst + n * 1024));
+  }
+}
+
 // Lane-constant parts of the transposing reads.  For rows d = D0 + lane % 32
 // (D0 a multiple of 32) and tokens T0 .. T0+15 (T0 a multiple of 16), MFMA
 // slot s of the lane holds token T0 + 8 (s / 4) + 4 half + s % 4 (the order in
