@@ -5,14 +5,13 @@
 // list), fed the way the forward kernel of attn_fwd_bf16.hip is fed:
 //
 //  * Every tile reaches LDS row-major (token rows of 256 bytes) by
-//    global_load_lds_dwordx4 (no VGPRs, no VALU): Q and dO in 64-query steps
-//    through a three-stage ring for dK/dV (one workgroup per CU; the DMA is
-//    issued from inline assembly so that only the kernel's own waits gate
-//    it), K and V in 32-key steps double-buffered for dQ (two workgroups per
-//    CU).
-//  * dK/dV uses 16x16x32 MFMAs throughout, so its one wave per SIMD always
-//    has eight independent score chains and sixteen independent dK / dV
-//    blocks in flight; dQ keeps 32x32x16 tiles.
+//    global_load_lds_dwordx4 (no VGPRs, no VALU) through three-stage rings,
+//    issued from inline assembly so that only the kernels' own waits gate
+//    the prefetch: Q and dO in 64-query steps for dK/dV (one workgroup per
+//    CU), K and V in 32-key steps for dQ (two workgroups per CU).
+//  * Both passes use 16x16x32 MFMAs throughout, so every wave has eight
+//    independent S / dP chains and sixteen independent dK / dV (or dQ)
+//    blocks in flight.
 //  * Products that contract over tokens need the tile transposed (dV^T +=
 //    dO^T.P, dK^T += Q^T.dS, dQ^T += K^T.dS^T).  Their A operands come from
 //    the same row-major tile through ds_read_b64_tr_b16: two transposing
@@ -317,22 +316,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
 }
 
 // --------------------------------------------------------------------- dQ
-// 32-key steps (two 8 KB tiles per stage, 33 KB of LDS): two workgroups per
-// CU, two waves per SIMD.
+// A wave owns 32 query rows (two 16-row halves qh) of one head and walks the
+// forward tile list in 32-key steps through a three-stage LDS ring (K, V and
+// subtree ends; two workgroups per CU).  S^T = K.Q^T and dP^T = V.dO^T are
+// eight independent 16x16 chains; dQ^T += K^T.dS^T sixteen blocks.
 constexpr int kQStep = 32;
 constexpr int kQBuf = kQStep * kRowB;  // 8 KB
+// stage layout: K tile | V tile | subtree ends [32]
+constexpr int kQStV = kQBuf, kQStSe = 2 * kQBuf;
+constexpr int kQStageB = 2 * kQBuf + 4 * kQStep;
 
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
     bf16_t* __restrict__ dq, TreeDev tr, int hq, int hkv, float c, float scale) {
-  using M = Mfma<bf16_t>;
-  __shared__ __attribute__((aligned(1024))) uint8_t k_l0[kQBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_l1[kQBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_l0[kQBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_l1[kQBuf];
-  __shared__ __attribute__((aligned(16))) int32_t sp_l0[kQStep];
-  __shared__ __attribute__((aligned(16))) int32_t sp_l1[kQStep];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kQStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kQStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kQStageB];
 
   const int G = hq / hkv;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -346,29 +346,39 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const int lq = lane % 32;
-  const int half = lane / 32;
-  const int qrow = qb * kTile + wave * 32 + lq;
+  const int li = lane % 16;  // query column of the 16x16 blocks
+  const int lg = lane / 16;  // 16-lane group: keys 4 lg .. 4 lg + 3 of each block
+  const int qlo = qb * kTile + wave * 32;
 
-  bf16x8_t qf[8], df[8];
-  {
-    const size_t off = (static_cast<size_t>(qrow) * hq + h) * D + half * 8;
+  // B operands Q^T / dO^T: query qlo + 16 qh + li, d = 32 s + 8 lg .. +7
+  bf16x8_t qf[2][4], df[2][4];
+  float lse2[2], dsq[2];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      qf[s] = M::load(q + off + 16 * s);
-      df[s] = M::load(dout + off + 16 * s);
+  for (int qh = 0; qh < 2; ++qh) {
+    const int row = qlo + 16 * qh + li;
+    const size_t off = (static_cast<size_t>(row) * hq + h) * D + 8 * lg;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      qf[qh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(q + off + 32 * s4));
+      df[qh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dout + off + 32 * s4));
     }
+    lse2[qh] = lse[static_cast<size_t>(h) * tr.Np + row] * kLog2e;
+    dsq[qh] = dsum[static_cast<size_t>(h) * tr.Np + row];
   }
-  const float lse2 = lse[static_cast<size_t>(h) * tr.Np + qrow] * kLog2e;
-  const float dsum_q = dsum[static_cast<size_t>(h) * tr.Np + qrow];
-  int roff[8];
+  // A operands K / V: key row li (+16 for the second key half), chunk 4 s + lg
+  int roff[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) roff[s] = lq * kRowB + (((2 * s + half) ^ rsw(lq)) << 4);
-  const TrOff tro = tr_offsets(lane);
+  for (int s4 = 0; s4 < 4; ++s4) roff[s4] = li * kRowB + (((4 * s4 + lg) ^ rsw(li)) << 4);
+  int trv;  // transposed K reads: lane i of group lg addresses key 4 lg + i / 4, d = 4 (i % 4) ..
+  {
+    const int t = 4 * lg + li / 4;
+    const int a = li % 4;
+    trv = t * kRowB + ((((a >> 1) ^ rsw(t))) << 4) + ((a & 1) << 3);
+  }
 
-  f32x16_t dqacc[4];
+  f32x4_t dqacc[8][2];  // (d block db, query half qh)
 #pragma unroll
-  for (int b = 0; b < 4; ++b) dqacc[b] = f32x16_t{};
+  for (int db = 0; db < 8; ++db) dqacc[db][0] = dqacc[db][1] = f32x4_t{};
 
   const uint32_t kv_bytes = static_cast<uint32_t>(hkv) * D * 2;
   const char* kgb = reinterpret_cast<const char*>(k + static_cast<size_t>(g) * D);
@@ -379,88 +389,111 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   const int t_begin = q_ptr[qb];
   const int n_steps = 4 * (q_ptr[qb + 1] - t_begin);  // four 32-key steps per tile
   auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + (st >> 2)); };
-  auto step_kb = [&](int st) { return q_tile[tile_of(st)] >> 1; };
+  auto step_key0 = [&](int st) { return (q_tile[tile_of(st)] >> 1) * kTile + kQStep * (st & 3); };
 
-  int se1 = 0;
-  auto issue_loads = [&](int st, uint8_t* kl, uint8_t* vl) {
-    const int k0 = step_kb(st) * kTile + kQStep * (st & 3);
-    // the subtree end first: its wait then leaves the DMA in flight
-    se1 = tr.se[k0 + (tid & 31)];
-    dma_tile<kQStep>(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kl, wave, lane);
-    dma_tile<kQStep>(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vl, wave, lane);
+  // Every wave issues kDmaOps tile DMA instructions per step; wave 0 also the
+  // subtree ends, first, so a wait for vmcnt(kDmaOps) lands every step but
+  // the newest.
+  constexpr int kDmaOps = 2 * (kQStep / 16);
+  auto issue_loads = [&](int st, uint8_t* stg) {
+    const int k0 = step_key0(st);
+    const uint32_t base = lds_addr(stg);
+    if (wave == 0 && lane < kQStep / 4) dma16_asm(tr.se + k0 + 4 * lane, base + kQStSe);
+    dma_tile_asm<kQStep>(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, base, wave, lane);
+    dma_tile_asm<kQStep>(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, base + kQStV, wave, lane);
   };
-  auto store_span = [&](int st, int32_t* spl) {
-    if (tid < kQStep) spl[tid] = se1 - (step_kb(st) * kTile + kQStep * (st & 3) + tid);
-  };
 
-  auto step = [&](int st, const uint8_t* kl, const uint8_t* vl, const int32_t* spl, uint8_t* nkl,
-                  uint8_t* nvl, int32_t* nspl) {
-    const int k0 = step_kb(st) * kTile + kQStep * (st & 3);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int st_next = st + 1 < n_steps ? st + 1 : st;
-    issue_loads(st_next, nkl, nvl);
+  auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
+    const int k0 = step_key0(st);
+    const uint8_t* kl = stg;
+    const uint8_t* vl = stg + kQStV;
+    const int32_t* sel = reinterpret_cast<const int32_t*>(stg + kQStSe);
+    // step st staged by every wave, step st-1's LDS reads returned; a plain
+    // s_barrier, since a workgroup fence would also drain the newer prefetch
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaOps) : "memory");
+    issue_loads(st + 2 < n_steps ? st + 2 : n_steps - 1, fill);
 
-    const uint32_t bits = static_cast<uint32_t>(q_cls[tile_of(st)]);
-    const int cls = (bits >> (2 * (4 * wave + (st & 3)))) & 3;
-    if (cls != 0) {
-      const int A = qrow - k0 - 4 * half;
-      // P^T (rows are keys, this lane's column is its query), dP^T = V.dO^T
-      f32x16_t p = f32x16_t{}, dp = f32x16_t{};
+    const uint32_t cls =
+        (static_cast<uint32_t>(q_cls[tile_of(st)]) >> (2 * (4 * wave + (st & 3)))) & 3;
+    if (cls == 0) return;
+    // S^T and dP^T blocks (key half kh, query half qh): eight chains
+    f32x4_t sacc[2][2], dpacc[2][2];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        p = M::mma(lds_frag(kl, roff[s]), qf[s], p);
-        dp = M::mma(lds_frag(vl, roff[s]), df[s], dp);
+    for (int kh = 0; kh < 2; ++kh) sacc[kh][0] = sacc[kh][1] = dpacc[kh][0] = dpacc[kh][1] = f32x4_t{};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const bf16x8_t ka = lds_frag(kl, kh * kHalf16 + roff[s4]);
+        const bf16x8_t va = lds_frag(vl, kh * kHalf16 + roff[s4]);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          sacc[kh][qh] = mma16(ka, qf[qh][s4], sacc[kh][qh]);
+          dpacc[kh][qh] = mma16(va, df[qh][s4], dpacc[kh][qh]);
+        }
       }
+    // P = exp(S c - LSE) on visible pairs, dS = P (dP - D); register i of
+    // block (kh, qh) is key k0 + 16 kh + 4 lg + i of query qlo + 16 qh + li
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      int sea[4] = {0, 0, 0, 0};
       if (cls == 1) {
+        const int4 sev = *reinterpret_cast<const int4*>(sel + 16 * kh + 4 * lg);
+        sea[0] = sev.x; sea[1] = sev.y; sea[2] = sev.z; sea[3] = sev.w;
+      }
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int4 sp = *reinterpret_cast<const int4*>(spl + 8 * i + 4 * half);
-          const int spv[4] = {sp.x, sp.y, sp.z, sp.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t dlt = static_cast<uint32_t>(A - (8 * i + j));
-            const float e = fast_exp2(fmaf(p[4 * i + j], c, -lse2));
-            p[4 * i + j] = dlt <= static_cast<uint32_t>(spv[j]) ? e : 0.f;
+          float e = fast_exp2(fmaf(sacc[kh][qh][i], c, -lse2[qh]));
+          if (cls == 1) {
+            const int key = k0 + 16 * kh + 4 * lg + i;
+            const uint32_t dlt = static_cast<uint32_t>(qlo + 16 * qh + li - key);
+            e = dlt <= static_cast<uint32_t>(sea[i] - key) ? e : 0.f;
           }
+          dpacc[kh][qh][i] = e * (dpacc[kh][qh][i] - dsq[qh]);
         }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(p[r], c, -lse2));
-      }
-      // dS^T = P^T (dP^T - D), dQ^T += K^T.dS^T
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] *= dp[r] - dsum_q;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8_t sf = M::from_acc(p, s2);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          dqacc[b] = M::mma(lds_tr_frag(kl, tro, 16 * s2, 32 * b), sf, dqacc[b]);
-      }
     }
-    store_span(st_next, nspl);
+    // dQ^T += K^T.dS^T
+    bf16x8_t sf[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) sf[qh] = pack8(dpacc[0][qh], dpacc[1][qh]);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8_t kt = lds_t16_frag(kl, trv, db);
+      dqacc[db][0] = mma16(kt, sf[0], dqacc[db][0]);
+      dqacc[db][1] = mma16(kt, sf[1], dqacc[db][1]);
+    }
   };
 
+  // the register loads above complete here (empty asm uses pin them before
+  // the loop), so no compiler wait inside the loop drains the prefetch
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    asm volatile("" ::"v"(lse2[qh]), "v"(dsq[qh]));
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) asm volatile("" ::"v"(qf[qh][s4]), "v"(df[qh][s4]));
+  }
   if (n_steps > 0) {
-    issue_loads(0, k_l0, v_l0);
-    store_span(0, sp_l0);
+    issue_loads(0, stage0);
+    issue_loads(1, stage1);  // n_steps >= 4
   }
-  for (int st = 0; st < n_steps; st += 2) {  // n_steps is a multiple of 4
-    step(st, k_l0, v_l0, sp_l0, k_l1, v_l1, sp_l1);
-    step(st + 1, k_l1, v_l1, sp_l1, k_l0, v_l0, sp_l0);
+  for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses stage st % 3
+    step(st, stage0, stage2);
+    if (st + 1 < n_steps) step(st + 1, stage1, stage0);
+    if (st + 2 < n_steps) step(st + 2, stage2, stage1);
   }
+  // the last steps' prefetch must land before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  bf16_t* op = dq + (static_cast<size_t>(qrow) * hq + h) * D;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int qh = 0; qh < 2; ++qh) {
+    bf16_t* op = dq + (static_cast<size_t>(qlo + 16 * qh + li) * hq + h) * D + 4 * lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = b * 32 + 8 * i + 4 * half;
-      store4<bf16_t>(op + d, dqacc[b][4 * i] * scale, dqacc[b][4 * i + 1] * scale,
-                     dqacc[b][4 * i + 2] * scale, dqacc[b][4 * i + 3] * scale);
-    }
+    for (int db = 0; db < 8; ++db)
+      store4<bf16_t>(op + 16 * db, dqacc[db][qh][0] * scale, dqacc[db][qh][1] * scale,
+                     dqacc[db][qh][2] * scale, dqacc[db][qh][3] * scale);
+  }
 }
 
 }  // namespace
