@@ -165,6 +165,8 @@ def main():
         b["lp"] = torch.empty(n_out_all, dtype=torch.float32, device=dev)
         b["ent"] = torch.empty(n_out_all, dtype=torch.float32, device=dev)
         if args.gather_bwd:
+            # (lse, entropy) per row, written by the forward gather, read by the backward
+            b["row_stats"] = torch.empty((Np_all, 2), dtype=torch.float32, device=dev)
             gen = torch.Generator(device=dev).manual_seed(w.seed + 99)
             b["dlp"] = torch.randn(n_out_all, generator=gen, device=dev)
             b["dent"] = torch.randn(n_out_all, generator=gen, device=dev)
@@ -188,7 +190,7 @@ def main():
             e[2].record(stream)
         if w.gather:
             pst.gather_tree_logprobs_entropy(b["logits"], m, logprobs=b["lp"], entropy=b["ent"],
-                                             stream=stream)
+                                             row_stats=b.get("row_stats"), stream=stream)
         if record:
             e[3].record(stream)
         if args.rope:
@@ -203,7 +205,8 @@ def main():
             if record:
                 e[4].record(stream)
             pst.gather_tree_logprobs_entropy_bwd(b["logits"], m, b["dlp"], b["dent"],
-                                                 dlogits=b["dlogits"], stream=stream)
+                                                 dlogits=b["dlogits"], row_stats=b["row_stats"],
+                                                 stream=stream)
             if record:
                 e[5].record(stream)
         return forest, [m], [e] if record else []
@@ -285,8 +288,8 @@ def main():
         if args.gather_bwd:
             gbw_t = sum(gbw_ms) / K * 1e-3
             # real rows read once + every row of d logits written + per output
-            # its two gradients, slot and target
-            gbw_bytes = (n_real + Np_all) * w.vocab * esz + n_out * 16 + 4 * (Np_all + 1)
+            # its two gradients, slot and target + the rows' saved statistics
+            gbw_bytes = (n_real + Np_all) * w.vocab * esz + n_out * 16 + 4 * (Np_all + 1) + 8 * n_real
             kernels["gather_bwd"] = {"ms_per_step": gbw_t * 1e3, "GB/s": gbw_bytes / gbw_t / 1e9,
                                      "launches_per_step": 1, "in_step": False}
 

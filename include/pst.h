@@ -232,10 +232,13 @@ int pst_tree_attn_bwd(const void* q, const void* k, const void* v, const void* o
  *   logits     device [Np, vocab] dtype (only the N real rows are read)
  *   logprobs   device float32 [n_out] (written)
  *   entropy    device float32 [n_out] (written)
- * Errors: PST_EINVAL, PST_EDTYPE, PST_EHIP. */
+ *   row_stats  device float32 [Np][2], 8-byte aligned, or NULL: when given,
+ *              (log-sum-exp, entropy) of every real row is written (pad
+ *              rows untouched), for pst_gather_tree_logprobs_entropy_bwd
+ * Errors: PST_EINVAL, PST_EDTYPE, PST_ESHAPE, PST_EHIP. */
 int pst_gather_tree_logprobs_entropy(const void* logits, int64_t vocab, int32_t dtype,
                                      const pst_tree_meta* meta, float* logprobs,
-                                     float* entropy, void* stream);
+                                     float* entropy, float* row_stats, void* stream);
 
 /* Gradient of the gather: d logits of
  *   sum_k dlogprobs[k] * logprobs[k] + dentropy[k] * entropy[k]
@@ -245,16 +248,21 @@ int pst_gather_tree_logprobs_entropy(const void* logits, int64_t vocab, int32_t 
  *   dx_v = -p_v (A + B (log p_v + H)) + sum_{k: t_k = v} dlogprobs[k],
  *   A = sum over outputs with a next token of dlogprobs, B = sum of dentropy,
  * p = softmax(x), H its entropy (a zero probability contributes 0).  Each
- * real row is read twice (statistics, then gradient) and written once; rows
- * no output reads (pad rows) are written as zeros.  Deterministic.
+ * real row is read once and written once when it fits a workgroup's
+ * registers (up to 32768 bf16 / 16384 fp32 entries) or when row_stats is
+ * given; otherwise twice (statistics, then gradient).  Rows no output reads
+ * (pad rows) are written as zeros.  Deterministic.
  *   logits     device [Np, vocab] dtype
  *   dlogprobs  device float32 [n_out], dentropy device float32 [n_out]
+ *   row_stats  NULL, or the row statistics that the forward gather wrote for
+ *              these same logits (device float32 [Np][2], 8-byte aligned)
  *   dlogits    device [Np, vocab] dtype (written), same alignment as logits
  *              modulo 16 bytes
  * Errors: PST_EINVAL, PST_EDTYPE, PST_ESHAPE, PST_EHIP. */
 int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int32_t dtype,
                                          const pst_tree_meta* meta, const float* dlogprobs,
-                                         const float* dentropy, void* dlogits, void* stream);
+                                         const float* dentropy, const float* row_stats,
+                                         void* dlogits, void* stream);
 
 /* ---- device: tree-position rotary embedding -------------------------------- */
 

@@ -86,9 +86,10 @@ _SIGS = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
                                     c_int32, c_int32, c_int32, c_int32, c_float, c_void_p]),
     "pst_gather_tree_logprobs_entropy": (c_int32, [c_void_p, c_int64, c_int32, c_void_p,
-                                                   c_void_p, c_void_p, c_void_p]),
+                                                   c_void_p, c_void_p, c_void_p, c_void_p]),
     "pst_gather_tree_logprobs_entropy_bwd": (c_int32, [c_void_p, c_int64, c_int32, c_void_p,
-                                                       c_void_p, c_void_p, c_void_p, c_void_p]),
+                                                       c_void_p, c_void_p, c_void_p, c_void_p,
+                                                       c_void_p]),
     "pst_tree_rope": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float, c_int32,
                                 c_void_p]),
     "pst_pack_allocate": (c_int32, [P64, c_int32, c_int64, c_int32, c_int32, c_int32, P32, P32,

@@ -42,6 +42,10 @@ def _stream_ptr(stream) -> int:
     return int(stream.cuda_stream)
 
 
+def _ptr_or_null(t):
+    return 0 if t is None else t.data_ptr()
+
+
 def _dev_tensor(t, name):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -231,7 +235,21 @@ def tree_attn_bwd(q, k, v, o, lse, dout, meta: TreeMeta, softmax_scale: Optional
     return dq, dk, dv
 
 
-def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=None, stream=None):
+def _row_stats(t, meta, name="row_stats"):
+    import torch
+    if t is None:
+        return None
+    _dev_tensor(t, name)
+    if t.dtype != torch.float32 or tuple(t.shape) != (meta.n_padded, 2):
+        raise ValueError(f"{name} must be float32 [{meta.n_padded}, 2]")
+    return t
+
+
+def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=None,
+                                 row_stats=None, stream=None):
+    """Per-sequence logprobs and entropies.  row_stats (optional, float32
+    [Np, 2]) receives (log-sum-exp, entropy) of every real row, which the
+    backward can take instead of re-reading each row for them."""
     import torch
     _dev_tensor(logits, "logits")
     if logits.dim() != 2 or logits.shape[0] != meta.n_padded:
@@ -244,14 +262,15 @@ def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=
     check(_lib.load().pst_gather_tree_logprobs_entropy(
         logits.data_ptr(), int(logits.shape[1]), _dtype_code(logits), meta._h,
         _dev_tensor(logprobs, "logprobs").data_ptr(), _dev_tensor(entropy, "entropy").data_ptr(),
-        c_void_p(_stream_ptr(stream))))
+        c_void_p(_ptr_or_null(_row_stats(row_stats, meta))), c_void_p(_stream_ptr(stream))))
     return logprobs, entropy
 
 
 def gather_tree_logprobs_entropy_bwd(logits, meta: TreeMeta, dlogprobs, dentropy, dlogits=None,
-                                     stream=None):
+                                     row_stats=None, stream=None):
     """d logits of sum(dlogprobs * logprobs + dentropy * entropy); returns
-    dlogits [Np, V] in the logits' dtype (pad rows zero)."""
+    dlogits [Np, V] in the logits' dtype (pad rows zero).  row_stats: the
+    forward gather's row statistics for these logits (optional)."""
     import torch
     _dev_tensor(logits, "logits")
     if logits.dim() != 2 or logits.shape[0] != meta.n_padded:
@@ -266,8 +285,9 @@ def gather_tree_logprobs_entropy_bwd(logits, meta: TreeMeta, dlogprobs, dentropy
         raise ValueError("dlogits must match logits in shape and dtype")
     check(_lib.load().pst_gather_tree_logprobs_entropy_bwd(
         logits.data_ptr(), int(logits.shape[1]), _dtype_code(logits), meta._h,
-        dlogprobs.data_ptr(), dentropy.data_ptr(), _dev_tensor(dlogits, "dlogits").data_ptr(),
-        c_void_p(_stream_ptr(stream))))
+        dlogprobs.data_ptr(), dentropy.data_ptr(),
+        c_void_p(_ptr_or_null(_row_stats(row_stats, meta))),
+        _dev_tensor(dlogits, "dlogits").data_ptr(), c_void_p(_stream_ptr(stream))))
     return dlogits
 
 

@@ -510,7 +510,7 @@ int pst_tree_attn_bwd(const void* q, const void* k, const void* v, const void* o
 
 int pst_gather_tree_logprobs_entropy(const void* logits, int64_t vocab, int32_t dtype,
                                      const pst_tree_meta* meta, float* logprobs,
-                                     float* entropy, void* stream) {
+                                     float* entropy, float* row_stats, void* stream) {
   if (!meta) return fail(PST_EINVAL, "tree metadata is NULL");
   if (dtype != PST_F32 && dtype != PST_BF16)
     return fail(PST_EDTYPE, "unknown dtype " + std::to_string(dtype));
@@ -523,16 +523,19 @@ int pst_gather_tree_logprobs_entropy(const void* logits, int64_t vocab, int32_t 
   const size_t esz = dtype == PST_BF16 ? 2 : 4;
   if (reinterpret_cast<uintptr_t>(logits) % esz)
     return fail(PST_ESHAPE, "logits pointer is not aligned to its element size");
+  if (reinterpret_cast<uintptr_t>(row_stats) % 8)
+    return fail(PST_ESHAPE, "row_stats pointer is not 8-byte aligned");
   if (int e = check_meta_device(meta)) return e;
   const hipError_t e = pst::launch_gather(dtype, logits, vocab, meta->dev, logprobs, entropy,
-                                          static_cast<hipStream_t>(stream));
+                                          row_stats, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   return ok();
 }
 
 int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int32_t dtype,
                                          const pst_tree_meta* meta, const float* dlogprobs,
-                                         const float* dentropy, void* dlogits, void* stream) {
+                                         const float* dentropy, const float* row_stats,
+                                         void* dlogits, void* stream) {
   if (!meta) return fail(PST_EINVAL, "tree metadata is NULL");
   if (dtype != PST_F32 && dtype != PST_BF16)
     return fail(PST_EDTYPE, "unknown dtype " + std::to_string(dtype));
@@ -548,9 +551,11 @@ int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int3
     return fail(PST_ESHAPE, "logits or dlogits pointer is not aligned to its element size");
   if ((reinterpret_cast<uintptr_t>(logits) - reinterpret_cast<uintptr_t>(dlogits)) % 16)
     return fail(PST_ESHAPE, "logits and dlogits must share their alignment modulo 16 bytes");
+  if (reinterpret_cast<uintptr_t>(row_stats) % 8)
+    return fail(PST_ESHAPE, "row_stats pointer is not 8-byte aligned");
   if (int e = check_meta_device(meta)) return e;
   const hipError_t e = pst::launch_gather_bwd(dtype, logits, vocab, meta->dev, dlogprobs, dentropy,
-                                              dlogits, static_cast<hipStream_t>(stream));
+                                              row_stats, dlogits, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gather backward launch");
   return ok();
 }

@@ -96,7 +96,8 @@ constexpr int kUnroll = 8;  // 16-byte chunks in flight per thread
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ logits, int64_t V,
                                                           TreeDev tr, float* __restrict__ logprobs,
-                                                          float* __restrict__ entropy) {
+                                                          float* __restrict__ entropy,
+                                                          float* __restrict__ stats_out) {
   constexpr int EPC = 16 / sizeof(T);
   __shared__ Acc part[kThreads / kWave];
   __shared__ float row_stats[2];
@@ -163,6 +164,9 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
     const float lse = r.m + fast_log2(r.s) * kLn2;
     row_stats[0] = lse;
     row_stats[1] = lse - r.t / r.s;
+    if (stats_out)  // (lse, entropy) of the row, for the backward
+      *reinterpret_cast<float2*>(stats_out + 2 * static_cast<size_t>(row)) =
+          make_float2(row_stats[0], row_stats[1]);
   }
   __syncthreads();
   const float lse = row_stats[0];
@@ -181,8 +185,9 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const T* __restrict__ 
 // (next token t_k, or none at a sequence's last position) gets
 //   dx_v = -p_v (A + B (log p_v + H)) + sum_{k: t_k = v} dlogprob_k,
 //   A = sum_{k with a next token} dlogprob_k,  B = sum_k dentropy_k.
-// Pass 1 streams the row for (lse, H) exactly as the forward does; pass 2
-// streams it again (mostly from cache) and writes -p_v (A + B (log p_v + H));
+// Pass 1 streams the row for (lse, H) exactly as the forward does (or, with
+// STATS, takes them as the forward saved them and only sums A and B); pass 2
+// streams it (again) and writes -p_v (A + B (log p_v + H));
 // then each distinct target of the row is rewritten once with its one-hot
 // terms added, so every element is rounded to the output type once.  Rows no
 // output reads (pad rows) are zero-filled.
@@ -215,10 +220,11 @@ __device__ __forceinline__ float grad_base(float x, float lse, float H, float A,
   return p > 0.f ? -p * fmaf(B, logp + H, A) : 0.f;
 }
 
-template <typename T, int TPB>
+template <typename T, int TPB, bool STATS>
 __global__ __launch_bounds__(TPB) void gather_bwd_kernel(
     const T* __restrict__ logits, int64_t V, TreeDev tr, const float* __restrict__ dlogprobs,
-    const float* __restrict__ dentropy, T* __restrict__ dlogits) {
+    const float* __restrict__ dentropy, const float* __restrict__ stats_in,
+    T* __restrict__ dlogits) {
   constexpr int EPC = 16 / sizeof(T);
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   __shared__ Acc part[TPB / kWave];
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(TPB) void gather_bwd_kernel(
   const uint32_t ninf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
   const u32x4_t pad = {ninf, ninf, ninf, ninf};
   Acc a{-INFINITY, 0.f, 0.f};
-  for (int64_t base = 0; base < nch; base += kUnroll * TPB) {
+  for (int64_t base = 0; base < (STATS ? 0 : nch); base += kUnroll * TPB) {
     u32x4_t u[kUnroll];
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
@@ -271,11 +277,11 @@ __global__ __launch_bounds__(TPB) void gather_bwd_kernel(
     }
     absorb(a, f);
   }
-  for (int64_t e = tid; e < head; e += TPB) {
+  for (int64_t e = tid; e < (STATS ? 0 : head); e += TPB) {
     float f[1] = {to_f32<T>(x[e])};
     absorb(a, f);
   }
-  for (int64_t e = tail0 + tid; e < V; e += TPB) {
+  for (int64_t e = tail0 + tid; e < (STATS ? 0 : V); e += TPB) {
     float f[1] = {to_f32<T>(x[e])};
     absorb(a, f);
   }
@@ -306,9 +312,15 @@ __global__ __launch_bounds__(TPB) void gather_bwd_kernel(
       A += sums[0][w];
       B += sums[1][w];
     }
-    const float lse = r.m + fast_log2(r.s) * kLn2;
-    row_stats[0] = lse;
-    row_stats[1] = lse - r.t / r.s;
+    if (STATS) {
+      const float2 st = *reinterpret_cast<const float2*>(stats_in + 2 * static_cast<size_t>(row));
+      row_stats[0] = st.x;
+      row_stats[1] = st.y;
+    } else {
+      const float lse = r.m + fast_log2(r.s) * kLn2;
+      row_stats[0] = lse;
+      row_stats[1] = lse - r.t / r.s;
+    }
     row_stats[2] = A;
     row_stats[3] = B;
   }
@@ -474,15 +486,15 @@ __global__ __launch_bounds__(TPB) void gather_bwd_resident_kernel(
 }  // namespace
 
 hipError_t launch_gather(int dtype, const void* logits, int64_t vocab, const TreeDev& tr,
-                         float* logprobs, float* entropy, hipStream_t stream) {
+                         float* logprobs, float* entropy, float* row_stats, hipStream_t stream) {
   if (tr.Np == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(tr.Np));  // pad rows exit at once
   if (dtype == kDtypeBf16)
     hipLaunchKernelGGL(gather_kernel<bf16_t>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const bf16_t*>(logits), vocab, tr, logprobs, entropy);
+                       static_cast<const bf16_t*>(logits), vocab, tr, logprobs, entropy, row_stats);
   else
     hipLaunchKernelGGL(gather_kernel<float>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const float*>(logits), vocab, tr, logprobs, entropy);
+                       static_cast<const float*>(logits), vocab, tr, logprobs, entropy, row_stats);
   return hipGetLastError();
 }
 
@@ -491,16 +503,17 @@ hipError_t launch_gather(int dtype, const void* logits, int64_t vocab, const Tre
 namespace pst {
 
 hipError_t launch_gather_bwd(int dtype, const void* logits, int64_t vocab, const TreeDev& tr,
-                             const float* dlogprobs, const float* dentropy, void* dlogits,
-                             hipStream_t stream) {
+                             const float* dlogprobs, const float* dentropy, const float* row_stats,
+                             void* dlogits, hipStream_t stream) {
   if (tr.Np == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(tr.Np));
   const size_t esz = dtype == kDtypeBf16 ? 2 : 4;
   // rows that are whole 16-byte chunks and fit a workgroup's registers (up
   // to 4096 chunks: 32768 bf16 or 16384 fp32 entries) are read once; larger
-  // rows take the two-pass kernel with 1024 threads per row, which keeps
-  // few enough rows in flight for their second read to hit the fabric-side
-  // cache
+  // rows are read once too when the forward's row statistics are given, and
+  // otherwise take the two-pass kernel with 1024 threads per row, which
+  // keeps few enough rows in flight for their second read to hit the
+  // fabric-side cache
   const bool aligned = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && (vocab * esz) % 16 == 0;
   const int64_t nch = static_cast<int64_t>(vocab * esz / 16);
   auto launch = [&](auto kern, int tpb, auto tag) {
@@ -508,16 +521,25 @@ hipError_t launch_gather_bwd(int dtype, const void* logits, int64_t vocab, const
     hipLaunchKernelGGL(kern, grid, dim3(tpb), 0, stream, static_cast<const T*>(logits), vocab, tr,
                        dlogprobs, dentropy, static_cast<T*>(dlogits));
   };
+  auto launch2 = [&](auto kern, int tpb, auto tag) {
+    using T = decltype(tag);
+    hipLaunchKernelGGL(kern, grid, dim3(tpb), 0, stream, static_cast<const T*>(logits), vocab, tr,
+                       dlogprobs, dentropy, row_stats, static_cast<T*>(dlogits));
+  };
   if (dtype == kDtypeBf16) {
     if (aligned && nch <= 256 * 16)
       launch(gather_bwd_resident_kernel<bf16_t, 256, 16>, 256, bf16_t{});
+    else if (row_stats)
+      launch2(gather_bwd_kernel<bf16_t, 512, true>, 512, bf16_t{});
     else
-      launch(gather_bwd_kernel<bf16_t, 1024>, 1024, bf16_t{});
+      launch2(gather_bwd_kernel<bf16_t, 1024, false>, 1024, bf16_t{});
   } else {
     if (aligned && nch <= 256 * 16)
       launch(gather_bwd_resident_kernel<float, 256, 16>, 256, float{});
+    else if (row_stats)
+      launch2(gather_bwd_kernel<float, 512, true>, 512, float{});
     else
-      launch(gather_bwd_kernel<float, 1024>, 1024, float{});
+      launch2(gather_bwd_kernel<float, 1024, false>, 1024, float{});
   }
   return hipGetLastError();
 }

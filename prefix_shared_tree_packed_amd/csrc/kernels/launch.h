@@ -39,13 +39,14 @@ hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v
                                      void* workspace, const TreeDev& tr, int hq, int hkv, float scale,
                                      hipStream_t stream);
 
+// row_stats (nullable): float [Np][2], (lse, entropy) of every real row.
 hipError_t launch_gather(int dtype, const void* logits, int64_t vocab, const TreeDev& tr,
-                         float* logprobs, float* entropy, hipStream_t stream);
+                         float* logprobs, float* entropy, float* row_stats, hipStream_t stream);
 
 // dlogits [Np, vocab] (dtype) from dlogprobs / dentropy (float32 [n_out]).
 hipError_t launch_gather_bwd(int dtype, const void* logits, int64_t vocab, const TreeDev& tr,
-                             const float* dlogprobs, const float* dentropy, void* dlogits,
-                             hipStream_t stream);
+                             const float* dlogprobs, const float* dentropy, const float* row_stats,
+                             void* dlogits, hipStream_t stream);
 
 // In-place rotary embedding of x [Np, heads, head_dim] with pos = depth
 // (inverse: the opposite rotation, the backward).

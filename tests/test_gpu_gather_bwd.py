@@ -126,3 +126,70 @@ def test_gather_bwd_rejects_misaligned_pair(gpu_lib):
         assert e.value.name == "PST_ESHAPE"
     finally:
         case.close()
+
+
+@pytest.mark.parametrize("vocab,dtype", [(40000, "bf16"), (20011, "f32"), (3001, "bf16")])
+def test_gather_bwd_with_forward_row_stats(gpu_lib, vocab, dtype):
+    """The forward's saved (lse, entropy) per row: checked against the oracle's
+    row statistics, then fed to the backward (rows beyond the register-resident
+    size take the one-read path), which must match the oracle as without them."""
+    import torch
+    rng = np.random.default_rng(vocab)
+    seqs = prompt_groups(rng, 3, 40, 3, 10, 90, vocab=500)
+    case = Case(seqs, 256)
+    try:
+        for t, tree in enumerate(case.ref.trees):
+            print(f"gather row stats case: dtype={dtype} V={vocab} tree={t}", flush=True)
+            meta = case.metas[t]
+            logits = make_tensor((tree.n_padded, vocab), dtype, vocab + t, "cuda", std=2.0)
+            stats = torch.zeros((tree.n_padded, 2), dtype=torch.float32, device="cuda")
+            gpu_lib.gather_tree_logprobs_entropy(logits, meta, row_stats=stats)
+            N = tree.n_tokens
+            lse, ent = oracle.row_lse_entropy(host(logits)[:N])
+            st = host(stats)
+            assert np.abs(st[:N, 0] - lse).max() <= 1e-4 * np.abs(lse).max() + 1e-5
+            assert np.abs(st[:N, 1] - ent).max() <= 1e-4 * np.abs(ent).max() + 1e-5
+            n = int(tree.out_offsets[-1])
+            g = torch.Generator(device="cpu").manual_seed(vocab + 7 + t)
+            dlp = torch.randn(n, generator=g, dtype=torch.float32).cuda()
+            dh = torch.randn(n, generator=g, dtype=torch.float32).cuda()
+            dx = gpu_lib.gather_tree_logprobs_entropy_bwd(logits, meta, dlp, dh, row_stats=stats)
+            ref = oracle.gather_logprobs_entropy_bwd(tree, seqs, host(logits), host(dlp), host(dh))
+            _check_rows(host(dx), ref, dtype, f"dlogits tree {t} (row stats)")
+            assert (host(dx)[N:] == 0).all()
+    finally:
+        case.close()
+
+
+def test_gather_bwd_bimodal_sampled_row_stats(gpu_lib):
+    """Full-size bimodal trees (152064-entry rows) through the forward with
+    row statistics and the one-read backward, sampled rows against the oracle."""
+    import torch
+    w = get_workload("bimodal")
+    case = Case(w.seqs, w.max_tokens_per_mb)
+    rng = np.random.default_rng(4)
+    try:
+        tree = case.ref.trees[0]
+        meta = case.metas[0]
+        print(f"gather bwd sampled: bimodal tree=0 N={tree.n_tokens}", flush=True)
+        logits = make_tensor((tree.n_padded, w.vocab), w.dtype, tree_tensor_seed(w.seed, 0, "logits"),
+                             "cuda", std=w.logit_std)
+        stats = torch.empty((tree.n_padded, 2), dtype=torch.float32, device="cuda")
+        gpu_lib.gather_tree_logprobs_entropy(logits, meta, row_stats=stats)
+        n = int(tree.out_offsets[-1])
+        g = torch.Generator(device="cpu").manual_seed(99)
+        dlp = torch.randn(n, generator=g, dtype=torch.float32).cuda()
+        dh = torch.randn(n, generator=g, dtype=torch.float32).cuda()
+        dx = gpu_lib.gather_tree_logprobs_entropy_bwd(logits, meta, dlp, dh, row_stats=stats)
+        torch.cuda.synchronize()
+        kids = np.diff(tree.child_ptr[:tree.n_tokens + 1])
+        branch = np.nonzero(kids > 1)[0]
+        rows = sorted(set(rng.choice(tree.n_tokens, size=8, replace=False).tolist())
+                      | set(branch[:4].tolist()) | {tree.n_tokens - 1})
+        lg = {r: host(logits[r]) for r in rows}
+        ref = oracle.gather_logprobs_entropy_bwd(tree, w.seqs, lg, host(dlp), host(dh), rows=rows)
+        for r in rows:
+            _check_rows(host(dx[r])[None], ref[r][None], w.dtype, f"dlogits row {r}")
+        assert int((dx[tree.n_tokens:] != 0).sum()) == 0
+    finally:
+        case.close()
