@@ -224,12 +224,19 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
     h[o_blk + 2 * b] = *std::min_element(se, se + 32);
     h[o_blk + 2 * b + 1] = *std::max_element(se, se + 32);
   }
-  // longest-processing-time orders over every block of every tree
+  // Work orders over every block of every tree.  Query blocks (forward and
+  // dQ): grouped by their first key block, so that the blocks resident on an
+  // XCD at one time share their prompt's K/V in L2, heaviest first within a
+  // group (longest processing time); measured 3-4 % faster than one global
+  // heaviest-first order.  Key blocks (dK/dV): heaviest first.
   {
     std::vector<int32_t> ord(nb);
     std::iota(ord.begin(), ord.end(), 0);
     const int32_t* qp = h + o_qptr;
+    const int32_t* qt = h + o_qtile;
+    auto minkb = [&](int32_t a) { return qt[qp[a + 1] - 1] >> 1; };
     std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
+      if (minkb(a) != minkb(b)) return minkb(a) < minkb(b);
       return qp[a + 1] - qp[a] > qp[b + 1] - qp[b];
     });
     std::copy(ord.begin(), ord.end(), h + o_ford);
