@@ -47,7 +47,8 @@ def kernel_sources(kernel, dtype, head_dim):
              "attn_bwd": ["attn_bwd_bf16.hip" if fast else "attn_bwd.hip"],
              "gather": ["gather.hip"]}[kernel]
     shared = ["common.h", "mfma.h"] + (["lds_tiles.h"] if fast and kernel != "gather" else [])
-    return [os.path.join(KDIR, f) for f in files + shared]
+    # the metadata layout and the device work orders are built in capi.cpp
+    return [os.path.join(KDIR, f) for f in files + shared] + [os.path.join(KDIR, "..", "capi.cpp")]
 
 
 def sources_sha256(paths):

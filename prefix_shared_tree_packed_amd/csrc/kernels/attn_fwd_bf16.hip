@@ -15,8 +15,7 @@
 //    three-stage LDS ring: while the waves compute one step, the K and V rows
 //    and subtree ends of the step after next stream global -> LDS directly
 //    (global_load_lds_dwordx4: no VGPRs, no VALU) into row-major tiles
-//    (swizzle of lds_tiles.h); one barrier per step.  Two steps of lead
-//    hide the load latency under full traffic, which one step did not.
+//    (swizzle of lds_tiles.h); one barrier per step, two steps in flight.
 //    48 KB of LDS and at most 168 VGPRs let three workgroups share a CU.
 //  * K rows are the A operand of S^T = K.Q^T as they stand (one 16-byte read
 //    per operand, shared by the two 16-query halves); the V^T operands of
