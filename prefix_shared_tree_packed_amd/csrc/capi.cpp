@@ -24,7 +24,10 @@ struct pst_forest {
 // se [Np] | q_ptr [nb+1] | q_tile [n_tiles] | kb_qhi [nb] | fwd_order [nb] |
 // bwd_order [nb] | row_out_ptr [Np+1] | out_pos [n_out] | out_tgt [n_out] |
 // blk32 [Np/32][2] (min, max subtree end of each 32-key block) |
-// q_cls [n_tiles] (32x32 sub-block classes of each tile) | pos [Np] (depth
+// q_cls [n_tiles] (32x32 sub-block classes of each tile) | step_ptr [nb+1] |
+// steps [n_steps] (the non-empty 32-key columns of each query block's
+// tiles: (32-key block << 8) | the four 32-query sub-blocks' classes) |
+// pos [Np] (depth
 // of every row, 0 for pad rows), every section starting on a 16-byte
 // boundary.  The pinned staging copy is
 // kept until destroy so the asynchronous upload never reads freed memory.
@@ -130,11 +133,19 @@ float resolve_scale(float s, int32_t head_dim) {
 // follow theirs.  Attention never crosses trees, so the concatenation is
 // itself a valid packed layout and one launch serves all of them.
 int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tree_meta** out) {
-  int64_t Np = 0, nb = 0, n_tiles = 0, n_out = 0;
+  int64_t Np = 0, nb = 0, n_tiles = 0, n_out = 0, n_steps = 0;
   pst_tree_sizes sz{};
+  // the four 32-query sub-blocks' classes of column ks of a tile
+  auto column_classes = [](int32_t bits, int ks) {
+    int32_t c4 = 0;
+    for (int qs = 0; qs < 4; ++qs) c4 |= ((bits >> (2 * (4 * qs + ks))) & 3) << (2 * qs);
+    return c4;
+  };
   for (const pst::Tree* t : trees) {
     pst_tree_sizes ts{};
     fill_sizes(*t, &ts);
+    for (int32_t bits : t->q_cls)
+      for (int ks = 0; ks < 4; ++ks) n_steps += column_classes(bits, ks) != 0;
     Np += t->Np;
     nb += t->nb;
     n_tiles += t->n_tiles();
@@ -166,6 +177,8 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   const size_t o_otgt = off;      off += round4(n_out);
   const size_t o_blk = off;       off += round4(Np / 16);
   const size_t o_qcls = off;      off += round4(n_tiles);
+  const size_t o_sptr = off;      off += round4(nb + 1);
+  const size_t o_step = off;      off += round4(n_steps);
   const size_t o_pos = off;       off += round4(Np);
   const size_t words = off;
 
@@ -219,6 +232,18 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   }
   h[o_qptr + nb] = tile0;
   h[o_rptr + Np] = out0;
+  {  // compacted step lists: a column every wave of the query block skips is not staged
+    int32_t ns = 0;
+    for (int64_t qb = 0; qb < nb; ++qb) {
+      h[o_sptr + qb] = ns;
+      for (int32_t ti = h[o_qptr + qb]; ti < h[o_qptr + qb + 1]; ++ti)
+        for (int ks = 0; ks < 4; ++ks) {
+          const int32_t c4 = column_classes(h[o_qcls + ti], ks);
+          if (c4) h[o_step + ns++] = (((h[o_qtile + ti] >> 1) * 4 + ks) << 8) | c4;
+        }
+    }
+    h[o_sptr + nb] = ns;
+  }
   for (int64_t b = 0; b < Np / 32; ++b) {
     const int32_t* se = h + o_se + 32 * b;
     h[o_blk + 2 * b] = *std::min_element(se, se + 32);
@@ -260,7 +285,8 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   int32_t* d = m->dbuf;
   m->dev = pst::TreeDev{d + o_se,   d + o_qptr, d + o_qtile, d + o_qhi,  d + o_ford,
                         d + o_bord, d + o_rptr, d + o_opos,  d + o_otgt, d + o_blk, d + o_qcls,
-                        d + o_pos,  sz.n_tokens, sz.n_padded, sz.n_blocks, sz.n_tiles};
+                        d + o_pos,  d + o_sptr, d + o_step, sz.n_tokens, sz.n_padded,
+                        sz.n_blocks, sz.n_tiles};
   *out = m;
   return ok();
 }

@@ -317,8 +317,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
 
 // --------------------------------------------------------------------- dQ
 // A wave owns 32 query rows (two 16-row halves qh) of one head and walks the
-// forward tile list in 32-key steps through a three-stage LDS ring (K, V and
-// subtree ends; two workgroups per CU).  S^T = K.Q^T and dP^T = V.dO^T are
+// query block's non-empty 32-key columns through a three-stage LDS ring (K, V
+// and subtree ends; two workgroups per CU).  S^T = K.Q^T and dP^T = V.dO^T are
 // eight independent 16x16 chains; dQ^T += K^T.dS^T sixteen blocks.
 constexpr int kQStep = 32;
 constexpr int kQBuf = kQStep * kRowB;  // 8 KB
@@ -383,13 +383,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   const uint32_t kv_bytes = static_cast<uint32_t>(hkv) * D * 2;
   const char* kgb = reinterpret_cast<const char*>(k + static_cast<size_t>(g) * D);
   const char* vgb = reinterpret_cast<const char*>(v + static_cast<size_t>(g) * D);
-  cint32* q_ptr = cst(tr.q_ptr);
-  cint32* q_tile = cst(tr.q_tile);
-  cint32* q_cls = cst(tr.q_cls);
-  const int t_begin = q_ptr[qb];
-  const int n_steps = 4 * (q_ptr[qb + 1] - t_begin);  // four 32-key steps per tile
-  auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + (st >> 2)); };
-  auto step_key0 = [&](int st) { return (q_tile[tile_of(st)] >> 1) * kTile + kQStep * (st & 3); };
+  // the query block's non-empty 32-key columns (scalar metadata reads)
+  cint32* steps = cst(tr.steps) + cst(tr.step_ptr)[qb];
+  const int n_steps = cst(tr.step_ptr)[qb + 1] - cst(tr.step_ptr)[qb];
+  auto step_key0 = [&](int st) { return (steps[st] >> 8) * kQStep; };
 
   // Every wave issues kDmaOps tile DMA instructions per step; wave 0 also the
   // subtree ends, first, so a wait for vmcnt(kDmaOps) lands every step but
@@ -413,8 +410,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaOps) : "memory");
     issue_loads(st + 2 < n_steps ? st + 2 : n_steps - 1, fill);
 
-    const uint32_t cls =
-        (static_cast<uint32_t>(q_cls[tile_of(st)]) >> (2 * (4 * wave + (st & 3)))) & 3;
+    const uint32_t cls = (static_cast<uint32_t>(steps[st]) >> (2 * wave)) & 3;
     if (cls == 0) return;
     // S^T and dP^T blocks (key half kh, query half qh): eight chains
     f32x4_t sacc[2][2], dpacc[2][2];
@@ -476,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   }
   if (n_steps > 0) {
     issue_loads(0, stage0);
-    issue_loads(1, stage1);  // n_steps >= 4
+    issue_loads(n_steps > 1 ? 1 : 0, stage1);
   }
   for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses stage st % 3
     step(st, stage0, stage2);

@@ -11,7 +11,8 @@
 //    independent 16x16 blocks.  S^T = K.Q^T puts one query in each lane
 //    column: a lane holds four keys of each block, so a query's row
 //    reductions span the four 16-lane groups (two permlane swaps).
-//  * Each non-empty 128x128 tile is walked in four 32-key steps through a
+//  * The non-empty 32-key columns of the query block's tiles (columns that
+//    no wave of the block sees are dropped by the host) are walked through a
 //    three-stage LDS ring: while the waves compute one step, the K and V rows
 //    and subtree ends of the step after next stream global -> LDS directly
 //    (global_load_lds_dwordx4: no VGPRs, no VALU) into row-major tiles
@@ -42,7 +43,6 @@ namespace {
 
 constexpr int D = 128;
 constexpr int kStep = 32;              // keys per pipeline step
-constexpr int kSpt = kTile / kStep;    // steps per tile
 constexpr int kKRow = D * 2;              // K row: 256 B
 constexpr int kBufBytes = kStep * kKRow;  // 8 KB for K, 8 KB for V
 constexpr int kHalfTile = 16 * kKRow;     // byte offset of keys 16..31 of a step tile
@@ -149,14 +149,10 @@ __global__ __launch_bounds__(256, 3) void tree_attn_fwd_bf16_d128(
   float m_used[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};  // this lane's share of each row sum
 
-  cint32* q_ptr = cst(tr.q_ptr);
-  cint32* q_tile = cst(tr.q_tile);
-  cint32* q_cls = cst(tr.q_cls);
-  const int t_begin = q_ptr[qb];
-  const int n_steps = kSpt * (q_ptr[qb + 1] - t_begin);
-  // tile index of a step, pinned to an SGPR so metadata reads stay scalar
-  auto tile_of = [&](int st) { return __builtin_amdgcn_readfirstlane(t_begin + st / kSpt); };
-  auto step_key0 = [&](int st) { return (q_tile[tile_of(st)] >> 1) * kTile + kStep * (st % kSpt); };
+  // the query block's non-empty 32-key columns (scalar metadata reads)
+  cint32* steps = cst(tr.steps) + cst(tr.step_ptr)[qb];
+  const int n_steps = cst(tr.step_ptr)[qb + 1] - cst(tr.step_ptr)[qb];
+  auto step_key0 = [&](int st) { return (steps[st] >> 8) * kStep; };
 
   // Staging of one step: the subtree ends of its keys (eight lanes of wave
   // 0) and its K and V rows, all global -> LDS.  Every wave issues kDmaOps
@@ -184,8 +180,7 @@ __global__ __launch_bounds__(256, 3) void tree_attn_fwd_bf16_d128(
     issue_loads(st + 2 < n_steps ? st + 2 : n_steps - 1, kfill, vfill, sfill);
 
     // class of this wave's 32x32 block: 0 empty, 1 partial, 2 full
-    const uint32_t cls =
-        (static_cast<uint32_t>(q_cls[tile_of(st)]) >> (2 * (4 * wave + st % kSpt))) & 3;
+    const uint32_t cls = (static_cast<uint32_t>(steps[st]) >> (2 * wave)) & 3;
     if (cls) {
       // S^T blocks (key half kh, query half qh): four independent chains
       f32x4_t sacc[2][2];
@@ -269,7 +264,7 @@ __global__ __launch_bounds__(256, 3) void tree_attn_fwd_bf16_d128(
 
   if (n_steps > 0) {
     issue_loads(0, k_lds0, v_lds0, se_lds0);
-    issue_loads(1, k_lds1, v_lds1, se_lds1);  // n_steps >= 4
+    issue_loads(n_steps > 1 ? 1 : 0, k_lds1, v_lds1, se_lds1);
   }
   for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses buffer st % 3
     step(st, k_lds0, v_lds0, se_lds0, k_lds2, v_lds2, se_lds2);

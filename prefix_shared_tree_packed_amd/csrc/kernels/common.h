@@ -37,6 +37,10 @@ struct TreeDev {
                                // sub-block qs, key sub-block ks at bit 2*(4*qs+ks)):
                                // 0 no visible pair, 1 some, 2 all
   const int32_t* pos;          // [Np] depth of every row (position id), 0 for pad rows
+  const int32_t* step_ptr;     // [nb+1] steps of each query block
+  const int32_t* steps;        // [n_steps] non-empty 32-key columns of the block's tiles:
+                               // (32-key block << 8) | class of 32-query sub-block qs
+                               // at bits 2 qs (0 no visible pair, 1 some, 2 all)
   int32_t N;
   int32_t Np;
   int32_t nb;
