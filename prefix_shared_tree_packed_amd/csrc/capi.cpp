@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <numeric>
@@ -27,6 +28,8 @@ struct pst_forest {
 // q_cls [n_tiles] (32x32 sub-block classes of each tile) | step_ptr [nb+1] |
 // steps [n_steps] (the non-empty 32-key columns of each query block's
 // tiles: (32-key block << 8) | the four 32-query sub-blocks' classes) |
+// unit_ptr [Np/32+1] | unit_steps [n_blk32] (the non-empty 32x32 blocks of
+// each 32-query unit: (32-key block << 2) | class) | unit_order [Np/32] |
 // pos [Np] (depth
 // of every row, 0 for pad rows), every section starting on a 16-byte
 // boundary.  The pinned staging copy is
@@ -133,7 +136,7 @@ float resolve_scale(float s, int32_t head_dim) {
 // follow theirs.  Attention never crosses trees, so the concatenation is
 // itself a valid packed layout and one launch serves all of them.
 int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tree_meta** out) {
-  int64_t Np = 0, nb = 0, n_tiles = 0, n_out = 0, n_steps = 0;
+  int64_t Np = 0, nb = 0, n_tiles = 0, n_out = 0, n_steps = 0, n_blk32 = 0;
   pst_tree_sizes sz{};
   // the four 32-query sub-blocks' classes of column ks of a tile
   auto column_classes = [](int32_t bits, int ks) {
@@ -145,7 +148,10 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
     pst_tree_sizes ts{};
     fill_sizes(*t, &ts);
     for (int32_t bits : t->q_cls)
-      for (int ks = 0; ks < 4; ++ks) n_steps += column_classes(bits, ks) != 0;
+      for (int ks = 0; ks < 4; ++ks) {
+        n_steps += column_classes(bits, ks) != 0;
+        for (int qs = 0; qs < 4; ++qs) n_blk32 += ((bits >> (2 * (4 * qs + ks))) & 3) != 0;
+      }
     Np += t->Np;
     nb += t->nb;
     n_tiles += t->n_tiles();
@@ -179,6 +185,9 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   const size_t o_qcls = off;      off += round4(n_tiles);
   const size_t o_sptr = off;      off += round4(nb + 1);
   const size_t o_step = off;      off += round4(n_steps);
+  const size_t o_uptr = off;      off += round4(Np / 32 + 1);
+  const size_t o_ustep = off;     off += round4(n_blk32);
+  const size_t o_uord = off;      off += round4(Np / 32);
   const size_t o_pos = off;       off += round4(Np);
   const size_t words = off;
 
@@ -243,6 +252,19 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
         }
     }
     h[o_sptr + nb] = ns;
+    // 32-query units: their non-empty 32x32 blocks, diagonal tile first
+    int32_t nu = 0;
+    for (int64_t u = 0; u < Np / 32; ++u) {
+      h[o_uptr + u] = nu;
+      const int64_t qb = u / 4;
+      const int qs = static_cast<int>(u % 4);
+      for (int32_t ti = h[o_qptr + qb]; ti < h[o_qptr + qb + 1]; ++ti)
+        for (int ks = 0; ks < 4; ++ks) {
+          const int32_t cls = (h[o_qcls + ti] >> (2 * (4 * qs + ks))) & 3;
+          if (cls) h[o_ustep + nu++] = (((h[o_qtile + ti] >> 1) * 4 + ks) << 2) | cls;
+        }
+    }
+    h[o_uptr + Np / 32] = nu;
   }
   for (int64_t b = 0; b < Np / 32; ++b) {
     const int32_t* se = h + o_se + 32 * b;
@@ -271,6 +293,23 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
       return qhi[a] - a > qhi[b] - b;
     });
     std::copy(ord.begin(), ord.end(), h + o_bord);
+    // 32-query units: the same grouping by first key block, most blocks first
+    std::vector<int32_t> uord(Np / 32);
+    std::iota(uord.begin(), uord.end(), 0);
+    const int32_t* up = h + o_uptr;
+    const int32_t* us = h + o_ustep;
+    auto ufirst = [&](int32_t a) {  // smallest 32-key block of the unit
+      int32_t m = INT32_MAX;
+      for (int32_t i = up[a]; i < up[a + 1]; ++i) m = std::min(m, us[i] >> 2);
+      return m;
+    };
+    std::vector<int32_t> first(uord.size());
+    for (size_t a = 0; a < uord.size(); ++a) first[a] = ufirst(static_cast<int32_t>(a));
+    std::stable_sort(uord.begin(), uord.end(), [&](int32_t a, int32_t b) {
+      if (first[a] / 4 != first[b] / 4) return first[a] / 4 < first[b] / 4;
+      return up[a + 1] - up[a] > up[b + 1] - up[b];
+    });
+    std::copy(uord.begin(), uord.end(), h + o_uord);
   }
   e = hipMemcpyAsync(m->dbuf, h, words * sizeof(int32_t), hipMemcpyHostToDevice,
                      static_cast<hipStream_t>(stream));
@@ -285,8 +324,8 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   int32_t* d = m->dbuf;
   m->dev = pst::TreeDev{d + o_se,   d + o_qptr, d + o_qtile, d + o_qhi,  d + o_ford,
                         d + o_bord, d + o_rptr, d + o_opos,  d + o_otgt, d + o_blk, d + o_qcls,
-                        d + o_pos,  d + o_sptr, d + o_step, sz.n_tokens, sz.n_padded,
-                        sz.n_blocks, sz.n_tiles};
+                        d + o_pos,  d + o_sptr, d + o_step, d + o_uptr, d + o_ustep,
+                        d + o_uord, sz.n_tokens, sz.n_padded, sz.n_blocks, sz.n_tiles};
   *out = m;
   return ok();
 }

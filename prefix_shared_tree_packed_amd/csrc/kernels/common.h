@@ -41,6 +41,10 @@ struct TreeDev {
   const int32_t* steps;        // [n_steps] non-empty 32-key columns of the block's tiles:
                                // (32-key block << 8) | class of 32-query sub-block qs
                                // at bits 2 qs (0 no visible pair, 1 some, 2 all)
+  const int32_t* unit_ptr;     // [Np/32+1] blocks of each 32-query unit
+  const int32_t* unit_steps;   // [n_blk32] non-empty 32x32 blocks of a unit:
+                               // (32-key block << 2) | class (1 some, 2 all)
+  const int32_t* unit_order;   // [Np/32] units, grouped by first key block
   int32_t N;
   int32_t Np;
   int32_t nb;

@@ -43,9 +43,13 @@ def test_fwd_tiny_workload(gpu_lib):
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("f32", 4, 2, 64), ("bf16", 8, 2, 128),
-                                             ("bf16", 5, 1, 64), ("bf16", 6, 6, 128)])
+                                             ("bf16", 5, 1, 64), ("bf16", 6, 6, 128),
+                                             ("bf16", 10, 2, 128), ("bf16", 12, 2, 128),
+                                             ("bf16", 16, 2, 128), ("bf16", 6, 2, 128)])
 def test_fwd_several_tiles(gpu_lib, dtype, hq, hkv, d):
-    """Trees spanning several 128-blocks with a ragged tail, several trees."""
+    """Trees spanning several 128-blocks with a ragged tail, several trees.
+    bf16 head_dim 128 with 4, 5, 6 or 8 query heads per key/value head runs
+    32-query units of several heads; 1 or 3 per group runs 128-query blocks."""
     rng = np.random.default_rng(hq * 7 + d)
     seqs = prompt_groups(rng, 3, 150, 3, 20, 260)
     _fwd_full(gpu_lib, seqs, 1024, hq, hkv, d, dtype, 10 + hq)
