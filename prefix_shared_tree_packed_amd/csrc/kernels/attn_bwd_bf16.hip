@@ -326,6 +326,10 @@ constexpr int kQBuf = kQStep * kRowB;  // 8 KB
 constexpr int kQStV = kQBuf, kQStSe = 2 * kQBuf;
 constexpr int kQStageB = 2 * kQBuf + 4 * kQStep;
 
+// UNIT = false: a workgroup is one 128-query block of one head; UNIT =
+// true: one 32-query unit of four heads of one key/value group (one wave per
+// head), walking the unit's non-empty 32x32 blocks.
+template <bool UNIT>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
@@ -336,19 +340,36 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
 
   const int G = hq / hkv;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_g = G * tr.nb;
-  const int g = logical / per_g;
-  const int rem = logical - g * per_g;
-  const int rank = rem / G;
-  const int h = g * G + (rem - rank * G);
-  const int qb = cst(tr.fwd_order)[rank];
-
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int li = lane % 16;  // query column of the 16x16 blocks
   const int lg = lane / 16;  // 16-lane group: keys 4 lg .. 4 lg + 3 of each block
-  const int qlo = qb * kTile + wave * 32;
+  int g, h, qlo, n_steps;
+  cint32* steps;
+  if constexpr (UNIT) {
+    const int per_unit = G / 4;  // workgroups per unit and group
+    const int per_g = per_unit * (tr.Np / 32);
+    g = logical / per_g;
+    const int rem = logical - g * per_g;
+    const int rank = rem / per_unit;
+    h = g * G + (rem - rank * per_unit) * 4 + wave;
+    const int u = cst(tr.unit_order)[rank];
+    qlo = u * 32;
+    steps = cst(tr.unit_steps) + cst(tr.unit_ptr)[u];
+    n_steps = cst(tr.unit_ptr)[u + 1] - cst(tr.unit_ptr)[u];
+  } else {
+    const int per_g = G * tr.nb;
+    g = logical / per_g;
+    const int rem = logical - g * per_g;
+    const int rank = rem / G;
+    h = g * G + (rem - rank * G);
+    const int qb = cst(tr.fwd_order)[rank];
+    qlo = qb * kTile + wave * 32;
+    // the query block's non-empty 32-key columns (scalar metadata reads)
+    steps = cst(tr.steps) + cst(tr.step_ptr)[qb];
+    n_steps = cst(tr.step_ptr)[qb + 1] - cst(tr.step_ptr)[qb];
+  }
 
   // B operands Q^T / dO^T: query qlo + 16 qh + li, d = 32 s + 8 lg .. +7
   bf16x8_t qf[2][4], df[2][4];
@@ -383,10 +404,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   const uint32_t kv_bytes = static_cast<uint32_t>(hkv) * D * 2;
   const char* kgb = reinterpret_cast<const char*>(k + static_cast<size_t>(g) * D);
   const char* vgb = reinterpret_cast<const char*>(v + static_cast<size_t>(g) * D);
-  // the query block's non-empty 32-key columns (scalar metadata reads)
-  cint32* steps = cst(tr.steps) + cst(tr.step_ptr)[qb];
-  const int n_steps = cst(tr.step_ptr)[qb + 1] - cst(tr.step_ptr)[qb];
-  auto step_key0 = [&](int st) { return (steps[st] >> 8) * kQStep; };
+  auto step_key0 = [&](int st) { return (steps[st] >> (UNIT ? 2 : 8)) * kQStep; };
 
   // Every wave issues kDmaOps tile DMA instructions per step; wave 0 also the
   // subtree ends, first, so a wait for vmcnt(kDmaOps) lands every step but
@@ -410,7 +428,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaOps) : "memory");
     issue_loads(st + 2 < n_steps ? st + 2 : n_steps - 1, fill);
 
-    const uint32_t cls = (static_cast<uint32_t>(steps[st]) >> (2 * wave)) & 3;
+    const uint32_t cls = UNIT ? static_cast<uint32_t>(steps[st]) & 3
+                              : (static_cast<uint32_t>(steps[st]) >> (2 * wave)) & 3;
     if (cls == 0) return;
     // S^T and dP^T blocks (key half kh, query half qh): eight chains
     f32x4_t sacc[2][2], dpacc[2][2];
@@ -516,10 +535,19 @@ hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v
                      static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), tr, hq, hkv, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_bf16, dim3(static_cast<unsigned>(tr.nb) * hq), dim3(256), 0, stream,
-                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum,
-                     static_cast<bf16_t*>(dq), tr, hq, hkv, c, scale);
+  // dQ in 32-query units of four heads when the group size is a multiple
+  // of four, as the forward
+  if ((hq / hkv) % 4 == 0)
+    hipLaunchKernelGGL(bwd_dq_bf16<true>, dim3(static_cast<unsigned>(tr.Np / 32) * (hq / 4)),
+                       dim3(256), 0, stream, static_cast<const bf16_t*>(q),
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                       static_cast<const bf16_t*>(dout), lse, dsum, static_cast<bf16_t*>(dq), tr, hq,
+                       hkv, c, scale);
+  else
+    hipLaunchKernelGGL(bwd_dq_bf16<false>, dim3(static_cast<unsigned>(tr.nb) * hq), dim3(256), 0,
+                       stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum,
+                       static_cast<bf16_t*>(dq), tr, hq, hkv, c, scale);
   return hipGetLastError();
 }
 
