@@ -106,13 +106,16 @@ __device__ __forceinline__ void dma_step_rows(const char* src, uint32_t stride, 
   }
 }
 
-// UNIT = false: a workgroup is one 128-query block of one head (four waves
-// of 32 queries) and walks the block's non-empty 32-key columns.
-// UNIT = true: a workgroup is one 32-query unit of NW heads of one key/value
-// group (one wave per head, same queries) and walks the unit's non-empty
-// 32x32 blocks: every wave has work in every step, and the staged K/V tile
-// serves NW heads.
-template <bool UNIT, int NW>
+// A unit workgroup is one 32-query unit of NW heads of one key/value group
+// (one wave per head, same queries) and walks the unit's non-empty 32x32
+// blocks: every wave has work in every step, and the staged K/V tile serves
+// NW heads.  A block workgroup is one 128-query block of one head (four
+// waves of 32 queries) and walks the block's non-empty 32-key columns.
+// MODE 0: 128-query blocks only; 1: units only (heads per group a multiple
+// of four); 2: mixed, for a group size G = 4 m + r: the first workgroups
+// are units of the group's first 4 m heads, the rest 128-query blocks of
+// its last r heads.
+template <int MODE, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     bf16_t* __restrict__ o, float* __restrict__ lse, TreeDev tr, int hq, int hkv, float c) {
@@ -137,13 +140,19 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
   const int lane = tid % kWave;
   const int li = lane % 16;  // query column of the 16x16 blocks
   const int lg = lane / 16;  // 16-lane group: keys 4 lg .. 4 lg + 3 of each block
-  int g, h, qlo, n_steps;
+  // logical work ids run group by group (so each XCD keeps one group's K/V
+  // in its L2): first the group's units, then its 128-query blocks
+  const int G4 = MODE == 0 ? 0 : G / NW * NW;  // heads of each group served by units
+  const int GR = G - G4;                       // heads served by 128-query blocks
+  const int per_unit = G4 / NW;                // unit workgroups per unit and group
+  const int u_g = per_unit * (tr.Np / 32);
+  const int per_g = u_g + GR * tr.nb;
+  const int g = logical / per_g;
+  const int rem = logical - g * per_g;
+  const bool UNIT = rem < u_g;
+  int h, qlo, n_steps;
   cint32* steps;
-  if constexpr (UNIT) {
-    const int per_unit = G / NW;  // workgroups per unit and group
-    const int per_g = per_unit * (tr.Np / 32);
-    g = logical / per_g;
-    const int rem = logical - g * per_g;
+  if (UNIT) {
     const int rank = rem / per_unit;
     h = g * G + (rem - rank * per_unit) * NW + wave;
     const int u = cst(tr.unit_order)[rank];
@@ -151,11 +160,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
     steps = cst(tr.unit_steps) + cst(tr.unit_ptr)[u];
     n_steps = cst(tr.unit_ptr)[u + 1] - cst(tr.unit_ptr)[u];
   } else {
-    const int per_g = G * tr.nb;
-    g = logical / per_g;
-    const int rem = logical - g * per_g;
-    const int rank = rem / G;
-    h = g * G + (rem - rank * G);
+    const int rb = rem - u_g;
+    const int rank = rb / GR;
+    h = g * G + G4 + (rb - rank * GR);
     const int qb = cst(tr.fwd_order)[rank];
     qlo = qb * kTile + wave * 32;  // first query row of this wave
     // the query block's non-empty 32-key columns (scalar metadata reads)
@@ -194,7 +201,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
   float m_used[2] = {-INFINITY, -INFINITY};
   float l_part[2] = {0.f, 0.f};  // this lane's share of each row sum
 
-  auto step_key0 = [&](int st) { return (steps[st] >> (UNIT ? 2 : 8)) * kStep; };
+  const int step_shift = UNIT ? 2 : 8;
+  auto step_key0 = [&](int st) { return (steps[st] >> step_shift) * kStep; };
 
   // Staging of one step: the subtree ends of its keys (eight lanes of wave
   // 0) and its K and V rows, all global -> LDS.  Every wave issues kDmaOps
@@ -343,16 +351,23 @@ hipError_t launch_attn_fwd_bf16_d128(const void* q, const void* k, const void* v
   const auto* kp = static_cast<const bf16_t*>(k);
   const auto* vp = static_cast<const bf16_t*>(v);
   auto* op = static_cast<bf16_t*>(o);
-  // 32-query units of four heads when the group size is a multiple of four
-  // (measured 11 % faster than 128-query blocks at four heads per group, 2 %
-  // at eight); otherwise 128-query blocks of one head
+  // 32-query units of four heads for as many heads of each group as a
+  // multiple of four covers (measured 11 % faster than 128-query blocks at
+  // four heads per group, 2 % at eight); 128-query blocks of one head for
+  // the rest
   const unsigned units = static_cast<unsigned>(tr.Np / 32);
-  if (G % 4 == 0)
-    hipLaunchKernelGGL((tree_attn_fwd_bf16_d128<true, 4>), dim3(units * (hq / 4)), dim3(256), 0,
-                       stream, qp, kp, vp, op, lse, tr, hq, hkv, c);
+  const unsigned nb = static_cast<unsigned>(tr.nb);
+  const unsigned G4 = G / 4 * 4, GR = G - G4;
+  const dim3 grid(hkv * ((G4 / 4) * units + GR * nb));
+  if (GR == 0)
+    hipLaunchKernelGGL((tree_attn_fwd_bf16_d128<1, 4>), grid, dim3(256), 0, stream, qp, kp, vp, op,
+                       lse, tr, hq, hkv, c);
+  else if (G4 > 0)
+    hipLaunchKernelGGL((tree_attn_fwd_bf16_d128<2, 4>), grid, dim3(256), 0, stream, qp, kp, vp, op,
+                       lse, tr, hq, hkv, c);
   else
-    hipLaunchKernelGGL((tree_attn_fwd_bf16_d128<false, 4>), dim3(static_cast<unsigned>(tr.nb) * hq),
-                       dim3(256), 0, stream, qp, kp, vp, op, lse, tr, hq, hkv, c);
+    hipLaunchKernelGGL((tree_attn_fwd_bf16_d128<0, 4>), grid, dim3(256), 0, stream, qp, kp, vp, op,
+                       lse, tr, hq, hkv, c);
   return hipGetLastError();
 }
 
