@@ -33,7 +33,10 @@ def test_fwd_worked_example_fp32(gpu_lib):
 
 
 def test_fwd_worked_example_bf16(gpu_lib):
+    # 4 and 5 query heads per key/value head: units of four heads, and units
+    # plus 128-query blocks for the fifth, on a single 128-row tree
     _fwd_full(gpu_lib, worked_example(), 128, 4, 1, 128, "bf16", 3)
+    _fwd_full(gpu_lib, worked_example(), 128, 5, 1, 128, "bf16", 5)
     _fwd_full(gpu_lib, worked_example(), 128, 2, 2, 64, "bf16", 4, scale=0.2)
 
 
@@ -218,9 +221,11 @@ def test_invalid_shapes_rejected(gpu_lib):
         case.close()
 
 
-def test_forest_meta_matches_per_tree(gpu_lib):
+@pytest.mark.parametrize("hq", [8, 10])
+def test_forest_meta_matches_per_tree(gpu_lib, hq):
     """One launch over the whole forest (trees back to back) gives bitwise
-    the same outputs and gradients as one launch per tree."""
+    the same outputs and gradients as one launch per tree (4 and 5 query
+    heads per key/value head)."""
     import torch
     rng = np.random.default_rng(21)
     seqs = prompt_groups(rng, 5, 200, 3, 30, 300)
@@ -230,7 +235,7 @@ def test_forest_meta_matches_per_tree(gpu_lib):
         fmeta = gpu_lib.forest_meta_create(case.forest)
         Np = sum(t.n_padded for t in case.ref.trees)
         assert fmeta.n_padded == Np
-        q, k, v, do = attn_inputs(Np, 8, 2, 128, "bf16", 60, with_dout=True)
+        q, k, v, do = attn_inputs(Np, hq, 2, 128, "bf16", 60, with_dout=True)
         o, lse = gpu_lib.tree_attn_fwd(q, k, v, fmeta)
         dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, fmeta)
         r0 = 0
