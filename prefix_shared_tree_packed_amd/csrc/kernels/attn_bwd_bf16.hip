@@ -185,18 +185,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
   // also one for LSE / D, first, so a wait for vmcnt(kDmaOps) lands every
   // step but the newest.
   constexpr int kDmaOps = 2 * (kKvStep / 16);
+  const TileOff<kKvStep> qoff = tile_offsets<kKvStep>(q_bytes, wave, lane);
   auto issue_loads = [&](int st, uint8_t* stg) {
     int qb, h, q0;
     decode(st, qb, h, q0);
     const size_t r0 = static_cast<size_t>(h) * tr.Np + q0;
     const uint32_t base = lds_addr(stg);
     if (wave == 0)
-      dma4_asm(lse + r0 + lane, base + kStLs);
+      dma4_s(lse + r0, 4u * lane, base + kStLs);
     else if (wave == 1)
-      dma4_asm(dsum + r0 + lane, base + kStDd);
+      dma4_s(dsum + r0, 4u * lane, base + kStDd);
     const size_t row0 = static_cast<size_t>(q0) * q_bytes + static_cast<size_t>(h) * D * 2;
-    dma_tile_asm<kKvStep>(reinterpret_cast<const char*>(q) + row0, q_bytes, base, wave, lane);
-    dma_tile_asm<kKvStep>(reinterpret_cast<const char*>(dout) + row0, q_bytes, base + kStDo, wave, lane);
+    dma_tile_s<kKvStep>(reinterpret_cast<const char*>(q) + row0, qoff, base, wave);
+    dma_tile_s<kKvStep>(reinterpret_cast<const char*>(dout) + row0, qoff, base + kStDo, wave);
   };
 
   auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
@@ -226,17 +227,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) sacc[a][b] = dpacc[a][b] = f32x4_t{};
+      // operand reads run one (s, q16) pair ahead of their MFMAs
+      bf16x8_t qa = lds_frag(qsl, roff[0]), da = lds_frag(dosl, roff[0]);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int q16 = 0; q16 < 2; ++q16) {
-          const bf16x8_t qa = lds_frag(qsl, q16 * kHalf16 + roff[s]);
-          const bf16x8_t da = lds_frag(dosl, q16 * kHalf16 + roff[s]);
+          bf16x8_t qn = qa, dn = da;
+          if (q16 == 0) {
+            qn = lds_frag(qsl, kHalf16 + roff[s]);
+            dn = lds_frag(dosl, kHalf16 + roff[s]);
+          } else if (s < 3) {
+            qn = lds_frag(qsl, roff[s + 1]);
+            dn = lds_frag(dosl, roff[s + 1]);
+          }
 #pragma unroll
           for (int kh = 0; kh < 2; ++kh) {
             sacc[q16][kh] = mma16(qa, kf[kh][s], sacc[q16][kh]);
             dpacc[q16][kh] = mma16(da, vf[kh][s], dpacc[q16][kh]);
           }
+          qa = qn;
+          da = dn;
         }
       // P = exp(S c - LSE) on visible pairs (register i of block (q16, kh) is
       // query qlo + 16 q16 + 4 lg + i, key kbase + 16 kh + li); dS = P (dP - D)
@@ -267,15 +278,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
         sf[kh] = pack8(dpacc[0][kh], dpacc[1][kh]);
       }
       // dV^T += dO^T.P, dK^T += Q^T.dS
+      bf16x8_t dot = lds_t16_frag(dosl, trv, 0), qt = lds_t16_frag(qsl, trv, 0);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const bf16x8_t dot = lds_t16_frag(dosl, trv, db);
-        const bf16x8_t qt = lds_t16_frag(qsl, trv, db);
+        bf16x8_t don = dot, qtn = qt;
+        if (db < 7) {
+          don = lds_t16_frag(dosl, trv, db + 1);
+          qtn = lds_t16_frag(qsl, trv, db + 1);
+        }
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
           dvacc[db][kh] = mma16(dot, pf[kh], dvacc[db][kh]);
           dkacc[db][kh] = mma16(qt, sf[kh], dkacc[db][kh]);
         }
+        dot = don;
+        qt = qtn;
       }
     }
   };
@@ -410,12 +427,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   // subtree ends, first, so a wait for vmcnt(kDmaOps) lands every step but
   // the newest.
   constexpr int kDmaOps = 2 * (kQStep / 16);
+  const TileOff<kQStep> koffs = tile_offsets<kQStep>(kv_bytes, wave, lane);
   auto issue_loads = [&](int st, uint8_t* stg) {
     const int k0 = step_key0(st);
     const uint32_t base = lds_addr(stg);
-    if (wave == 0 && lane < kQStep / 4) dma16_asm(tr.se + k0 + 4 * lane, base + kQStSe);
-    dma_tile_asm<kQStep>(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, base, wave, lane);
-    dma_tile_asm<kQStep>(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, base + kQStV, wave, lane);
+    if (wave == 0 && lane < kQStep / 4) dma16_s(tr.se + k0, 16u * lane, base + kQStSe);
+    dma_tile_s<kQStep>(kgb + static_cast<size_t>(k0) * kv_bytes, koffs, base, wave);
+    dma_tile_s<kQStep>(vgb + static_cast<size_t>(k0) * kv_bytes, koffs, base + kQStV, wave);
   };
 
   auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
@@ -435,17 +453,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     f32x4_t sacc[2][2], dpacc[2][2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) sacc[kh][0] = sacc[kh][1] = dpacc[kh][0] = dpacc[kh][1] = f32x4_t{};
+    // operand reads run one (s4, kh) pair ahead of their MFMAs
+    bf16x8_t ka = lds_frag(kl, roff[0]), va = lds_frag(vl, roff[0]);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        const bf16x8_t ka = lds_frag(kl, kh * kHalf16 + roff[s4]);
-        const bf16x8_t va = lds_frag(vl, kh * kHalf16 + roff[s4]);
+        bf16x8_t kn = ka, vn = va;
+        if (kh == 0) {
+          kn = lds_frag(kl, kHalf16 + roff[s4]);
+          vn = lds_frag(vl, kHalf16 + roff[s4]);
+        } else if (s4 < 3) {
+          kn = lds_frag(kl, roff[s4 + 1]);
+          vn = lds_frag(vl, roff[s4 + 1]);
+        }
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
           sacc[kh][qh] = mma16(ka, qf[qh][s4], sacc[kh][qh]);
           dpacc[kh][qh] = mma16(va, df[qh][s4], dpacc[kh][qh]);
         }
+        ka = kn;
+        va = vn;
       }
     // P = exp(S c - LSE) on visible pairs, dS = P (dP - D); register i of
     // block (kh, qh) is key k0 + 16 kh + 4 lg + i of query qlo + 16 qh + li
@@ -473,11 +501,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     bf16x8_t sf[2];
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) sf[qh] = pack8(dpacc[0][qh], dpacc[1][qh]);
+    bf16x8_t kt = lds_t16_frag(kl, trv, 0);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const bf16x8_t kt = lds_t16_frag(kl, trv, db);
+      bf16x8_t ktn = kt;
+      if (db < 7) ktn = lds_t16_frag(kl, trv, db + 1);
       dqacc[db][0] = mma16(kt, sf[0], dqacc[db][0]);
       dqacc[db][1] = mma16(kt, sf[1], dqacc[db][1]);
+      kt = ktn;
     }
   };
 

@@ -20,7 +20,14 @@
 //    and subtree ends of the step after next stream global -> LDS directly
 //    (global_load_lds_dwordx4: no VGPRs, no VALU) into row-major tiles
 //    (swizzle of lds_tiles.h); one barrier per step, two steps in flight.
-//    48 KB of LDS and at most 168 VGPRs let three workgroups share a CU.
+//    Each copy takes the step's base address in SGPRs and a lane offset
+//    fixed for the whole kernel, so staging costs no per-lane address
+//    arithmetic (the per-lane 64-bit form cost ~10 % of the kernel's time,
+//    VALU issue and registers).  48 KB of LDS and at most 168 VGPRs let
+//    three workgroups share a CU.
+//  * LDS operand reads run one fragment ahead of the MFMAs that use them
+//    (each MFMA pair waits for the read issued one pair earlier, not for
+//    the one just issued).
 //  * K rows are the A operand of S^T = K.Q^T as they stand (one 16-byte read
 //    per operand, shared by the two 16-query halves); the V^T operands of
 //    O^T += V^T.P^T come from the same row-major V tile through two
@@ -86,24 +93,6 @@ __device__ __forceinline__ bf16x8_t lds_vt_frag(const uint8_t* tile, int trv, in
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
   const i16x8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, w);
-}
-
-// K or V rows of one 32-key step, global -> LDS, over NW waves: eight
-// 1 KB instructions (4 rows each); with NW not dividing 8 the last waves
-// repeat an instruction of the first ones (same data, same place), so that
-// every wave issues the same count.
-template <int NW>
-__device__ __forceinline__ void dma_step_rows(const char* src, uint32_t stride, uint8_t* dst, int wave,
-                                              int lane) {
-#pragma unroll
-  for (int i = 0; i < (8 + NW - 1) / NW; ++i) {
-    int n = wave + NW * i;
-    if (n >= 8) n -= 8;
-    const int r = 4 * n + (lane >> 4);
-    const int cch = (lane & 15) ^ rsw(r);
-    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(r) * stride + (cch << 4),
-                                     (lds_void*)(dst + n * 1024), 16, 0, 0);
-  }
 }
 
 // A unit workgroup is one 32-query unit of NW heads of one key/value group
@@ -209,12 +198,31 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
   // DMA instructions per step (wave 0 one more, first), so a wait for
   // vmcnt(kDmaOps) lands every step but the newest.
   constexpr int kDmaOps = 2 * ((8 + NW - 1) / NW);
+  // per-lane byte offsets of this wave's rows within a step's K (or V)
+  // slice: eight 1 KB instructions of 4 rows each, over NW waves (with NW
+  // not dividing 8 the last waves repeat an instruction of the first ones:
+  // same data, same place, so every wave issues the same count)
+  constexpr int kRowOps = (8 + NW - 1) / NW;
+  uint32_t roff[kRowOps];
+  int rslot[kRowOps];
+#pragma unroll
+  for (int i = 0; i < kRowOps; ++i) {
+    int n = wave + NW * i;
+    if (n >= 8) n -= 8;
+    const int r = 4 * n + (lane >> 4);
+    roff[i] = static_cast<uint32_t>(r) * kv_bytes + ((((lane & 15) ^ rsw(r))) << 4);
+    rslot[i] = n * 1024;
+  }
   auto issue_loads = [&](int st, uint8_t* kdst, uint8_t* vdst, int32_t* sdst) {
     const int k0 = step_key0(st);
     if (wave == 0 && lane < kStep / 4)
-      __builtin_amdgcn_global_load_lds(tr.se + k0 + 4 * lane, (lds_void*)sdst, 16, 0, 0);
-    dma_step_rows<NW>(kgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, kdst, wave, lane);
-    dma_step_rows<NW>(vgb + static_cast<size_t>(k0) * kv_bytes, kv_bytes, vdst, wave, lane);
+      dma16_s(tr.se + k0, 16u * lane, lds_addr(sdst));
+    const char* kb = kgb + static_cast<size_t>(k0) * kv_bytes;
+    const char* vb = vgb + static_cast<size_t>(k0) * kv_bytes;
+#pragma unroll
+    for (int i = 0; i < kRowOps; ++i) dma16_s(kb, roff[i], lds_addr(kdst) + rslot[i]);
+#pragma unroll
+    for (int i = 0; i < kRowOps; ++i) dma16_s(vb, roff[i], lds_addr(vdst) + rslot[i]);
   };
 
   auto step = [&](int st, const uint8_t* kcur, const uint8_t* vcur, const int32_t* scur,
@@ -237,13 +245,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
       f32x4_t sacc[2][2];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) sacc[kh][0] = sacc[kh][1] = f32x4_t{};
+      bf16x8_t kf = lds_frag(kcur, koff[0]);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-          const bf16x8_t kf = lds_frag(kcur, kh * kHalfTile + koff[s]);
+          bf16x8_t kn = kf;
+          if (kh == 0) kn = lds_frag(kcur, kHalfTile + koff[s]);
+          else if (s < 3) kn = lds_frag(kcur, koff[s + 1]);
           sacc[kh][0] = mma16(kf, qf[0][s], sacc[kh][0]);
           sacc[kh][1] = mma16(kf, qf[1][s], sacc[kh][1]);
+          kf = kn;
         }
 
       // mask a partial block; row max of the raw scores (register i of block
@@ -304,11 +316,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
       }
 
       // O^T += V^T.P^T: sixteen independent blocks
+      bf16x8_t vf = lds_vt_frag(vcur, trv, 0);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const bf16x8_t vf = lds_vt_frag(vcur, trv, db);
+        bf16x8_t vn = vf;
+        if (db < 7) vn = lds_vt_frag(vcur, trv, db + 1);
         oacc[db][0] = mma16(vf, pf[0], oacc[db][0]);
         oacc[db][1] = mma16(vf, pf[1], oacc[db][1]);
+        vf = vn;
       }
     }
   };

@@ -21,53 +21,59 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 __device__ __forceinline__ int rsw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
-// NROWS token rows of 256 bytes (row stride `stride` bytes in memory) ->
-// swizzled LDS tile; the four waves issue NROWS / 16 DMA instructions each,
-// instruction n covering rows 4n .. 4n+3.
-template <int NROWS>
-__device__ __forceinline__ void dma_tile(const char* src, uint32_t stride, uint8_t* dst, int wave,
-                                         int lane) {
-#pragma unroll
-  for (int i = 0; i < NROWS / 16; ++i) {
-    const int n = (NROWS / 16) * wave + i;
-    const int r = 4 * n + (lane >> 4);
-    const int cch = (lane & 15) ^ rsw(r);
-    __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(r) * stride + (cch << 4),
-                                     (lds_void*)(dst + n * 1024), 16, 0, 0);
-  }
-}
-
-// Same staging as dma_tile, issued through inline assembly (M0 = LDS base),
-// so the compiler does not track it as an LDS store: it then inserts no
+// DMA staging, issued through inline assembly (M0 = LDS base), so the
+// compiler does not track it as an LDS store: it then inserts no
 // conservative vmcnt(0) before reads of other buffers, and the caller owns
 // every wait (vmcnt) and the barrier (whose "memory" clobber orders the LDS
-// reads after it).
+// reads after it).  Each copy takes a wave-uniform base address (an SGPR
+// pair) plus a 32-bit lane offset that stays fixed for the whole kernel, so
+// a step's staging costs no per-lane 64-bit address arithmetic.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (const __attribute__((address_space(3))) uint8_t*)(p)));
 }
-__device__ __forceinline__ void dma16_asm(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+// 16 bytes per lane: base + voff -> LDS lds_base + 16 * lane
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds_base), "v"(src)
+               : "s"(lds_base), "v"(voff), "s"(base)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4_asm(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+// 4 bytes per lane: base + voff -> LDS lds_base + 4 * lane
+__device__ __forceinline__ void dma4_s(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :
-               : "s"(lds_base), "v"(src)
+               : "s"(lds_base), "v"(voff), "s"(base)
                : "memory", "m0");
 }
+
+// NROWS token rows of 256 bytes (row stride `stride` bytes in memory) ->
+// swizzled LDS tile; the four waves issue NROWS / 16 DMA instructions each,
+// instruction n covering rows 4n .. 4n+3.  tile_offsets gives the lane's
+// byte offsets within the rows (computed once), dma_tile_s issues the copies
+// from a tile's first row `base`.
 template <int NROWS>
-__device__ __forceinline__ void dma_tile_asm(const char* src, uint32_t stride, uint32_t dst, int wave,
-                                             int lane) {
+struct TileOff {
+  uint32_t v[NROWS / 16];
+};
+template <int NROWS>
+__device__ __forceinline__ TileOff<NROWS> tile_offsets(uint32_t stride, int wave, int lane) {
+  TileOff<NROWS> o;
 #pragma unroll
   for (int i = 0; i < NROWS / 16; ++i) {
     const int n = (NROWS / 16) * wave + i;
     const int r = 4 * n + (lane >> 4);
-    const int cch = (lane & 15) ^ rsw(r);
-    dma16_asm(src + static_cast<size_t>(r) * stride + (cch << 4),
-              __builtin_amdgcn_readfirstlane(dst + n * 1024));
+    o.v[i] = static_cast<uint32_t>(r) * stride + (static_cast<uint32_t>((lane & 15) ^ rsw(r)) << 4);
+  }
+  return o;
+}
+template <int NROWS>
+__device__ __forceinline__ void dma_tile_s(const char* base, const TileOff<NROWS>& o, uint32_t dst,
+                                           int wave) {
+#pragma unroll
+  for (int i = 0; i < NROWS / 16; ++i) {
+    const int n = (NROWS / 16) * wave + i;
+    dma16_s(base, o.v[i], __builtin_amdgcn_readfirstlane(dst + n * 1024));
   }
 }
 
