@@ -159,14 +159,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
     n_steps = cst(tr.step_ptr)[qb + 1] - cst(tr.step_ptr)[qb];
   }
 
-  // B operands of S^T = K.Q^T: query qlo + 16 qh + li, d = 32 s + 8 lg .. +7
-  bf16x8_t qf[2][4];
-#pragma unroll
-  for (int qh = 0; qh < 2; ++qh) {
-    const bf16_t* qp = q + (static_cast<size_t>(qlo + 16 * qh + li) * hq + h) * D + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qf[qh][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 32 * s));
-  }
+  bf16x8_t qf[2][4];  // B operands of S^T = K.Q^T, loaded below
   // A operands: key row li (+16 for the second key half), chunk 4 s + lg
   int koff[4];
 #pragma unroll
@@ -332,6 +325,20 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
     issue_loads(0, k_lds0, v_lds0, se_lds0);
     issue_loads(n_steps > 1 ? 1 : 0, k_lds1, v_lds1, se_lds1);
   }
+  // query qlo + 16 qh + li, d = 32 s + 8 lg .. +7; loaded while the first
+  // two steps stream in, and completed here (empty asm uses pin them before
+  // the loop): the compiler does not count the assembly DMA, so its own
+  // waits for these loads, left inside the loop, would drain the prefetch
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    const bf16_t* qp = q + (static_cast<size_t>(qlo + 16 * qh + li) * hq + h) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[qh][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 32 * s));
+  }
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) asm volatile("" ::"v"(qf[qh][s]));
   for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses buffer st % 3
     step(st, k_lds0, v_lds0, se_lds0, k_lds2, v_lds2, se_lds2);
     if (st + 1 < n_steps) step(st + 1, k_lds1, v_lds1, se_lds1, k_lds0, v_lds0, se_lds0);
