@@ -57,6 +57,8 @@ constexpr int kKRow = D * 2;              // K row: 256 B
 constexpr int kBufBytes = kStep * kKRow;  // 8 KB for K, 8 KB for V
 constexpr int kHalfTile = 16 * kKRow;     // byte offset of keys 16..31 of a step tile
 constexpr float kRescale = 8.0f;          // lazy-rescale threshold (log2 units)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only: scalar loads
 
@@ -70,12 +72,26 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int byte_off) 
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + byte_off));
 }
 
-// Max / sum over the four lanes l % 16 + 16 g (g = 0..3) that hold one query.
-__device__ __forceinline__ float quad_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  return max_halves(y);
+// max without NaN quieting: the scores are finite or -inf, and permlane
+// results would otherwise be canonicalised first (two extra VALU ops each)
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Row maxima of both query halves at once: on entry x (y) holds each lane's
+// partial max of query half 0 (1); on return every lane holds, in x and y,
+// the max over the four lanes l % 16 + 16 g (g = 0..3) of its query.  Three
+// swaps serve both halves: after the first, rows 0, 2 carry x and rows 1, 3
+// carry y; the 32-lane swap folds rows 0 + 2 and 1 + 3; the last 16-lane
+// swap spreads x and y back over all four rows.
+__device__ __forceinline__ void quad_max2(float& x, float& y) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  const float m1 = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false, false);
+  const float m2 = vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(m2), __float_as_uint(m2), false, false);
+  x = __uint_as_float(c[0]);
+  y = __uint_as_float(c[1]);
 }
+// Sum over the four lanes l % 16 + 16 g (g = 0..3) that hold one query.
 __device__ __forceinline__ float quad_sum(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -181,6 +197,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
 #pragma unroll
   for (int db = 0; db < 8; ++db) oacc[db][0] = oacc[db][1] = f32x4_t{};
   float m_used[2] = {-INFINITY, -INFINITY};
+  float negm[2] = {0.f, 0.f};    // -m_used, 0 while m_used is -inf
   float l_part[2] = {0.f, 0.f};  // this lane's share of each row sum
 
   const int step_shift = UNIT ? 2 : 8;
@@ -270,42 +287,52 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
               const int span = sea[i] - (k0 + 4 * lg + 16 * kh + i);
               const float x = dlt <= static_cast<uint32_t>(span) ? sacc[kh][qh][i] : -INFINITY;
               sacc[kh][qh][i] = x;
-              m = fmaxf(m, x);
+              m = vmax(m, x);
             }
           } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[kh][qh][i]);
+            for (int i = 0; i < 4; ++i) m = vmax(m, sacc[kh][qh][i]);
           }
         }
-        mx[qh] = quad_max(m) * c;
+        mx[qh] = m;
       }
+      quad_max2(mx[0], mx[1]);
+      mx[0] *= c;
+      mx[1] *= c;
       if (__any(mx[0] > m_used[0] + kRescale || mx[1] > m_used[1] + kRescale)) {
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
-          const float m_new = fmaxf(m_used[qh], mx[qh]);
+          const float m_new = vmax(m_used[qh], mx[qh]);
           const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_used[qh] - m_new);
           l_part[qh] *= alpha;
 #pragma unroll
           for (int db = 0; db < 8; ++db) oacc[db][qh] *= alpha;
           m_used[qh] = m_new;
+          negm[qh] = m_new == -INFINITY ? 0.f : -m_new;
         }
       }
       bf16x8_t pf[2];
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
-        const float negm = m_used[qh] == -INFINITY ? 0.f : -m_used[qh];
         float e[8];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) e[4 * kh + i] = fast_exp2(fmaf(sacc[kh][qh][i], c, negm));
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) s += e[r];
-        l_part[qh] += s;
+          for (int i = 0; i < 4; ++i) e[4 * kh + i] = fast_exp2(fmaf(sacc[kh][qh][i], c, negm[qh]));
         typedef float f32x8_t __attribute__((ext_vector_type(8)));
         const f32x8_t ev = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
         pf[qh] = __builtin_convertvector(ev, bf16x8_t);
+        // row sum of the bf16 probabilities that O accumulates, two per
+        // v_dot2 against (1, 1).  (Written out with literal lane indices:
+        // taking the pairs as bit casts of a uint32 vector's elements was
+        // compiled into four reads of the first pair.)
+        const bf16x8_t& p8 = pf[qh];
+        float sum = l_part[qh];
+        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 0, 1), kOnes2, sum, false);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 2, 3), kOnes2, sum, false);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 4, 5), kOnes2, sum, false);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 6, 7), kOnes2, sum, false);
+        l_part[qh] = sum;
       }
 
       // O^T += V^T.P^T: sixteen independent blocks
