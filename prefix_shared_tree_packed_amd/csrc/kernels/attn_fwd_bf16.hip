@@ -245,12 +245,29 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
     // prefetch two steps ahead into the buffer step st-1 used; past the end
     // the last step again (in bounds, never read), so the code stays
     // branch-free and the count of outstanding DMA stays fixed
-    issue_loads(st + 2 < n_steps ? st + 2 : n_steps - 1, kfill, vfill, sfill);
+    const int k0p = step_key0(st + 2 < n_steps ? st + 2 : n_steps - 1);
+    if (wave == 0 && lane < kStep / 4) dma16_s(tr.se + k0p, 16u * lane, lds_addr(sfill));
+    const char* kbp = kgb + static_cast<size_t>(k0p) * kv_bytes;
+    const char* vbp = vgb + static_cast<size_t>(k0p) * kv_bytes;
+    // copy j of this wave's 2 kRowOps for the step (K rows, then V rows)
+    auto dma_op = [&](int j) {
+      if (j < kRowOps) dma16_s(kbp, roff[j], lds_addr(kfill) + rslot[j]);
+      else dma16_s(vbp, roff[j - kRowOps], lds_addr(vfill) + rslot[j - kRowOps]);
+    };
+    // Units (MODE 1) never hold an empty step: their copies are spread over
+    // the S^T MFMAs below, one per 32-deep slice, instead of leaving the
+    // barrier as one burst from every wave (measured 2 % faster).  Blocks
+    // issue them here, since a wave may skip the step.
+    static_assert(MODE != 1 || 2 * kRowOps == 4, "one copy per d slice");
+    if (MODE != 1) {
+#pragma unroll
+      for (int j = 0; j < 2 * kRowOps; ++j) dma_op(j);
+    }
 
     // class of this wave's 32x32 block: 0 empty, 1 partial, 2 full
     const uint32_t cls = UNIT ? static_cast<uint32_t>(steps[st]) & 3
                               : (static_cast<uint32_t>(steps[st]) >> (2 * wave)) & 3;
-    if (cls) {
+    if (MODE == 1 || cls) {
       // S^T blocks (key half kh, query half qh): four independent chains
       f32x4_t sacc[2][2];
 #pragma unroll
@@ -260,6 +277,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
+          if (MODE == 1 && kh == 1) dma_op(s);
           bf16x8_t kn = kf;
           if (kh == 0) kn = lds_frag(kcur, kHalfTile + koff[s]);
           else if (s < 3) kn = lds_frag(kcur, koff[s + 1]);
