@@ -286,32 +286,45 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
           kf = kn;
         }
 
-      // mask a partial block; row max of the raw scores (register i of block
-      // (kh, qh) is key 16 kh + 4 lg + i of query qlo + 16 qh + li)
+      // Mask a partial block: register i of block (kh, qh) is key
+      // j = kb + 16 kh + i (kb = k0 + 4 lg) of query q = qlo + 16 qh + li,
+      // and j sees q iff j <= q <= se[j].  With A = q - kb and S = se[j] - kb
+      // the second condition is A <= S (one compare per element, S formed
+      // once per key); the first holds for every pair off the diagonal
+      // block, and on it is a second pass, 16 kh + i <= A.
+      if (cls == 1) {
+        const int kb = k0 + 4 * lg;
+        const int4 s0 = *reinterpret_cast<const int4*>(scur + 4 * lg);
+        const int4 s1 = *reinterpret_cast<const int4*>(scur + 16 + 4 * lg);
+        const int S[2][4] = {{s0.x - kb, s0.y - kb, s0.z - kb, s0.w - kb},
+                             {s1.x - kb, s1.y - kb, s1.z - kb, s1.w - kb}};
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          const int A = qlo + 16 * qh + li - kb;
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[kh][qh][i] = A <= S[kh][i] ? sacc[kh][qh][i] : -INFINITY;
+        }
+        if (k0 + kStep > qlo) {
+#pragma unroll
+          for (int qh = 0; qh < 2; ++qh) {
+            const int A = qlo + 16 * qh + li - kb;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sacc[kh][qh][i] = 16 * kh + i <= A ? sacc[kh][qh][i] : -INFINITY;
+          }
+        }
+      }
+      // row max of the raw scores
       float mx[2];
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
-        float m = -INFINITY;
-        const int A = qlo + 16 * qh + li - k0 - 4 * lg;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          if (cls == 1) {
-            // key j sees query q iff (unsigned)(q - j) <= se[j] - j
-            const int4 sev = *reinterpret_cast<const int4*>(scur + 16 * kh + 4 * lg);
-            const int sea[4] = {sev.x, sev.y, sev.z, sev.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t dlt = static_cast<uint32_t>(A - (16 * kh + i));
-              const int span = sea[i] - (k0 + 4 * lg + 16 * kh + i);
-              const float x = dlt <= static_cast<uint32_t>(span) ? sacc[kh][qh][i] : -INFINITY;
-              sacc[kh][qh][i] = x;
-              m = vmax(m, x);
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) m = vmax(m, sacc[kh][qh][i]);
-          }
-        }
+        float m = vmax(sacc[0][qh][0], sacc[0][qh][1]);
+        m = vmax(vmax(m, sacc[0][qh][2]), sacc[0][qh][3]);
+        m = vmax(vmax(m, sacc[1][qh][0]), sacc[1][qh][1]);
+        m = vmax(vmax(m, sacc[1][qh][2]), sacc[1][qh][3]);
         mx[qh] = m;
       }
       quad_max2(mx[0], mx[1]);
