@@ -173,22 +173,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
   const uint32_t q_bytes = static_cast<uint32_t>(hq) * D * 2;  // one token's Q (or dO) rows
   const int qhi = cst(tr.kb_qhi)[kb];
   const int n_steps = (qhi - kb + 1) * G * 2;
-  // step -> (query block, head, half); steps walk halves, then heads, then blocks
-  auto decode = [&](int st, int& qb, int& h, int& q0) {
+  // step -> (query block, head of the group, half): steps walk halves, then
+  // heads, then blocks.  Cursors for the step being computed and the one
+  // being prefetched advance by one step at a time (divisions by the group
+  // size only here, outside the loop).
+  struct Cursor {
+    int qb, r, half;
+  };
+  auto cursor_at = [&](int st) {
     const int rest = st >> 1;
-    const int r = rest % G;
-    qb = kb + rest / G;
-    h = g * G + r;
-    q0 = qb * kTile + kKvStep * (st & 1);
+    return Cursor{kb + rest / G, rest % G, st & 1};
+  };
+  auto advance = [&](Cursor& cu) {
+    cu.half ^= 1;
+    if (cu.half == 0 && ++cu.r == G) {
+      cu.r = 0;
+      ++cu.qb;
+    }
+  };
+  auto decode = [&](const Cursor& cu, int& h, int& q0) {
+    h = g * G + cu.r;
+    q0 = cu.qb * kTile + kKvStep * cu.half;
   };
   // Every wave issues kDmaOps tile DMA instructions per step; waves 0 and 1
   // also one for LSE / D, first, so a wait for vmcnt(kDmaOps) lands every
   // step but the newest.
   constexpr int kDmaOps = 2 * (kKvStep / 16);
   const TileOff<kKvStep> qoff = tile_offsets<kKvStep>(q_bytes, wave, lane);
-  auto issue_loads = [&](int st, uint8_t* stg) {
-    int qb, h, q0;
-    decode(st, qb, h, q0);
+  auto issue_loads = [&](const Cursor& cu, uint8_t* stg) {
+    int h, q0;
+    decode(cu, h, q0);
     const size_t r0 = static_cast<size_t>(h) * tr.Np + q0;
     const uint32_t base = lds_addr(stg);
     if (wave == 0)
@@ -200,17 +214,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
     dma_tile_s<kKvStep>(reinterpret_cast<const char*>(dout) + row0, qoff, base + kStDo, wave);
   };
 
+  Cursor cur = cursor_at(0), pf = cursor_at(n_steps > 2 ? 2 : n_steps - 1);
   auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
     const uint8_t* ql = stg;
     const uint8_t* dol = stg + kStDo;
     const float* lsl = reinterpret_cast<const float*>(stg + kStLs);
     const float* ddl = reinterpret_cast<const float*>(stg + kStDd);
-    int qb, h, q0;
-    decode(st, qb, h, q0);
+    int h, q0;
+    decode(cur, h, q0);
+    advance(cur);
     // step st staged by every wave, step st-1's LDS reads returned; a plain
     // s_barrier, since a workgroup fence would also drain the newer prefetch
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaOps) : "memory");
-    issue_loads(st + 2 < n_steps ? st + 2 : n_steps - 1, fill);
+    // prefetch step min(st + 2, n_steps - 1)
+    issue_loads(pf, fill);
+    if (st + 3 < n_steps) advance(pf);
 
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
@@ -249,8 +267,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
           qa = qn;
           da = dn;
         }
-      // P = exp(S c - LSE) on visible pairs (register i of block (q16, kh) is
-      // query qlo + 16 q16 + 4 lg + i, key kbase + 16 kh + li); dS = P (dP - D)
+      // register i of block (q16, kh) is query qlo + 16 q16 + 4 lg + i, key
+      // kbase + 16 kh + li.  A partial block first sets its invisible scores
+      // to -inf (one branch per block, not a select per element of every
+      // block): key j sees query q iff (unsigned)(q - j) <= se[j] - j.
+      if (!full) {
+        const int A = qlo + 4 * lg - kbase - li;
+#pragma unroll
+        for (int q16 = 0; q16 < 2; ++q16)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t dlt = static_cast<uint32_t>(A + 16 * q16 + i - 16 * kh);
+              sacc[q16][kh][i] = dlt <= static_cast<uint32_t>(span_k[kh]) ? sacc[q16][kh][i] : -INFINITY;
+            }
+      }
+      // P = exp(S c - LSE), 0 where masked; dS = P (dP - D)
 #pragma unroll
       for (int q16 = 0; q16 < 2; ++q16) {
         const float4 l4 = *reinterpret_cast<const float4*>(lsl + 32 * qs + 16 * q16 + 4 * lg);
@@ -261,12 +294,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float e = fast_exp2(fmaf(sacc[q16][kh][i], c, -lv[i]));
-            if (!full) {
-              const uint32_t dlt =
-                  static_cast<uint32_t>(qlo + 16 * q16 + 4 * lg + i - (kbase + 16 * kh + li));
-              e = dlt <= static_cast<uint32_t>(span_k[kh]) ? e : 0.f;
-            }
+            const float e = fast_exp2(fmaf(sacc[q16][kh][i], c, -lv[i]));
             sacc[q16][kh][i] = e;
             dpacc[q16][kh][i] = e * (dpacc[q16][kh][i] - dd[i]);
           }
@@ -308,8 +336,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
     for (int s4 = 0; s4 < 4; ++s4) asm volatile("" ::"v"(kf[kh][s4]), "v"(vf[kh][s4]));
   }
   if (n_steps > 0) {
-    issue_loads(0, stage0);
-    issue_loads(1, stage1);  // n_steps >= 2
+    issue_loads(cursor_at(0), stage0);
+    issue_loads(cursor_at(1), stage1);  // n_steps >= 2
   }
   for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses stage st % 3
     step(st, stage0, stage2);
