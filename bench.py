@@ -47,8 +47,10 @@ def kernel_sources(kernel, dtype, head_dim):
              "attn_bwd": ["attn_bwd_bf16.hip" if fast else "attn_bwd.hip"],
              "gather": ["gather.hip"]}[kernel]
     shared = ["common.h", "mfma.h"] + (["lds_tiles.h"] if fast and kernel != "gather" else [])
-    # the metadata layout and the device work orders are built in capi.cpp
-    return [os.path.join(KDIR, f) for f in files + shared] + [os.path.join(KDIR, "..", "capi.cpp")]
+    # the metadata layout and the device work orders are built in capi.cpp;
+    # the compile flags (per file too) live in build.py
+    return ([os.path.join(KDIR, f) for f in files + shared] + [os.path.join(KDIR, "..", "capi.cpp")]
+            + [os.path.join(KDIR, "..", "..", "build.py")])
 
 
 def sources_sha256(paths):
