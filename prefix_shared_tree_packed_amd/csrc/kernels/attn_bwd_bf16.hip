@@ -503,28 +503,47 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
         ka = kn;
         va = vn;
       }
-    // P = exp(S c - LSE) on visible pairs, dS = P (dP - D); register i of
-    // block (kh, qh) is key k0 + 16 kh + 4 lg + i of query qlo + 16 qh + li
+    // Register i of block (kh, qh) is key j = kb + 16 kh + i (kb = k0 + 4 lg)
+    // of query q = qlo + 16 qh + li, and j sees q iff j <= q <= se[j].  A
+    // partial block first sets its invisible scores to -inf (one branch per
+    // step): with A = q - kb and S = se[j] - kb the second condition is
+    // A <= S; the first holds off the diagonal block and is a second pass
+    // on it, 16 kh + i <= A.
+    if (cls == 1) {
+      const int kb = k0 + 4 * lg;
+      const int4 s0 = *reinterpret_cast<const int4*>(sel + 4 * lg);
+      const int4 s1 = *reinterpret_cast<const int4*>(sel + 16 + 4 * lg);
+      const int S[2][4] = {{s0.x - kb, s0.y - kb, s0.z - kb, s0.w - kb},
+                           {s1.x - kb, s1.y - kb, s1.z - kb, s1.w - kb}};
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      int sea[4] = {0, 0, 0, 0};
-      if (cls == 1) {
-        const int4 sev = *reinterpret_cast<const int4*>(sel + 16 * kh + 4 * lg);
-        sea[0] = sev.x; sea[1] = sev.y; sea[2] = sev.z; sea[3] = sev.w;
+      for (int qh = 0; qh < 2; ++qh) {
+        const int A = qlo + 16 * qh + li - kb;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[kh][qh][i] = A <= S[kh][i] ? sacc[kh][qh][i] : -INFINITY;
       }
+      if (k0 + kQStep > qlo) {
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          const int A = qlo + 16 * qh + li - kb;
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[kh][qh][i] = 16 * kh + i <= A ? sacc[kh][qh][i] : -INFINITY;
+        }
+      }
+    }
+    // P = exp(S c - LSE), 0 where masked; dS = P (dP - D)
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float e = fast_exp2(fmaf(sacc[kh][qh][i], c, -lse2[qh]));
-          if (cls == 1) {
-            const int key = k0 + 16 * kh + 4 * lg + i;
-            const uint32_t dlt = static_cast<uint32_t>(qlo + 16 * qh + li - key);
-            e = dlt <= static_cast<uint32_t>(sea[i] - key) ? e : 0.f;
-          }
+          const float e = fast_exp2(fmaf(sacc[kh][qh][i], c, -lse2[qh]));
           dpacc[kh][qh][i] = e * (dpacc[kh][qh][i] - dsq[qh]);
         }
-    }
     // dQ^T += K^T.dS^T
     bf16x8_t sf[2];
 #pragma unroll
