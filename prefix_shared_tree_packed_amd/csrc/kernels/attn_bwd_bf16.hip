@@ -245,28 +245,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) sacc[a][b] = dpacc[a][b] = f32x4_t{};
-      // operand reads run one (s, q16) pair ahead of their MFMAs
-      bf16x8_t qa = lds_frag(qsl, roff[0]), da = lds_frag(dosl, roff[0]);
+      // operand reads run two (s, q16) pairs ahead of their MFMAs (one wave
+      // per SIMD: nothing else hides the LDS latency); the scheduling
+      // barrier keeps the compiler from sinking the reads back to their use
+      auto qoffs = [&](int f) { return ((f & 1) ? kHalf16 : 0) + roff[f >> 1]; };
+      bf16x8_t qbuf[3], dbuf[3];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int f = 0; f < 2; ++f) {
+        qbuf[f] = lds_frag(qsl, qoffs(f));
+        dbuf[f] = lds_frag(dosl, qoffs(f));
+      }
 #pragma unroll
-        for (int q16 = 0; q16 < 2; ++q16) {
-          bf16x8_t qn = qa, dn = da;
-          if (q16 == 0) {
-            qn = lds_frag(qsl, kHalf16 + roff[s]);
-            dn = lds_frag(dosl, kHalf16 + roff[s]);
-          } else if (s < 3) {
-            qn = lds_frag(qsl, roff[s + 1]);
-            dn = lds_frag(dosl, roff[s + 1]);
-          }
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            sacc[q16][kh] = mma16(qa, kf[kh][s], sacc[q16][kh]);
-            dpacc[q16][kh] = mma16(da, vf[kh][s], dpacc[q16][kh]);
-          }
-          qa = qn;
-          da = dn;
+      for (int f = 0; f < 8; ++f) {
+        if (f + 2 < 8) {
+          qbuf[(f + 2) % 3] = lds_frag(qsl, qoffs(f + 2));
+          dbuf[(f + 2) % 3] = lds_frag(dosl, qoffs(f + 2));
         }
+        __builtin_amdgcn_sched_barrier(0);
+        const int s = f >> 1, q16 = f & 1;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          sacc[q16][kh] = mma16(qbuf[f % 3], kf[kh][s], sacc[q16][kh]);
+          dpacc[q16][kh] = mma16(dbuf[f % 3], vf[kh][s], dpacc[q16][kh]);
+        }
+      }
       // register i of block (q16, kh) is query qlo + 16 q16 + 4 lg + i, key
       // kbase + 16 kh + li.  A partial block first sets its invisible scores
       // to -inf (one branch per block, not a select per element of every
@@ -306,21 +308,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
         sf[kh] = pack8(dpacc[0][kh], dpacc[1][kh]);
       }
       // dV^T += dO^T.P, dK^T += Q^T.dS
-      bf16x8_t dot = lds_t16_frag(dosl, trv, 0), qt = lds_t16_frag(qsl, trv, 0);
+      // transposed reads two d blocks ahead, held in place the same way
+      bf16x8_t obuf[3], tbuf[3];
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        obuf[db] = lds_t16_frag(dosl, trv, db);
+        tbuf[db] = lds_t16_frag(qsl, trv, db);
+      }
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        bf16x8_t don = dot, qtn = qt;
-        if (db < 7) {
-          don = lds_t16_frag(dosl, trv, db + 1);
-          qtn = lds_t16_frag(qsl, trv, db + 1);
+        if (db + 2 < 8) {
+          obuf[(db + 2) % 3] = lds_t16_frag(dosl, trv, db + 2);
+          tbuf[(db + 2) % 3] = lds_t16_frag(qsl, trv, db + 2);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-          dvacc[db][kh] = mma16(dot, pf[kh], dvacc[db][kh]);
-          dkacc[db][kh] = mma16(qt, sf[kh], dkacc[db][kh]);
+          dvacc[db][kh] = mma16(obuf[db % 3], pf[kh], dvacc[db][kh]);
+          dkacc[db][kh] = mma16(tbuf[db % 3], sf[kh], dkacc[db][kh]);
         }
-        dot = don;
-        qt = qtn;
       }
     }
   };
