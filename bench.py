@@ -182,6 +182,13 @@ def main():
         m = pst.forest_meta_create(forest, stream)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(8)] if record else None
         if record:
+            # The step is host-bound (tree build and metadata upload), so the
+            # GPU would reach e[0] idle and wait there for the forward's
+            # submission, timing the host's launch latency as kernel time.  A
+            # short spin (~0.1 ms, inside time the GPU would idle anyway)
+            # lets the host queue the forward first.  The later kernels of
+            # the step are queued while the forward runs.
+            torch.cuda._sleep(200000)
             e[0].record(stream)
         pst.tree_attn_fwd(b["q"], b["k"], b["v"], m, out=b["o"], lse=b["lse"], stream=stream)
         if record:
@@ -261,7 +268,7 @@ def main():
     fwd_flops = 4.0 * d * hq * pairs
     bwd_flops = 2.5 * fwd_flops if w.bwd else 0.0
     fwd_t = sum(fwd_ms) / K * 1e-3           # seconds of forward kernels per step
-    bwd_t = sum(bwd_ms) / K * 1e-3
+    bwd_t = sum(bwd_ms) / K * 1e-3 if w.bwd else 0.0  # (no kernel between the events otherwise)
     gat_t = sum(gat_ms) / K * 1e-3
     attn_tflops = (fwd_flops + bwd_flops) / (fwd_t + bwd_t) / 1e12
     kernels = {"attn_fwd": {"ms_per_step": fwd_t * 1e3, "TFLOP/s": fwd_flops / fwd_t / 1e12,
