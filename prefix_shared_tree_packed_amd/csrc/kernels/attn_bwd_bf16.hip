@@ -239,12 +239,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
       const uint8_t* qsl = ql + 32 * qs * kRowB;
       const uint8_t* dosl = dol + 32 * qs * kRowB;
 
-      // S and dP blocks (query half q16, key half kh): eight chains
+      // S and dP blocks (query half q16, key half kh): eight chains.  The
+      // dP accumulators start at -D (register i of block (q16, kh) is query
+      // qlo + 16 q16 + 4 lg + i), so the MFMAs leave dP - D and dS = P (dP - D)
+      // costs one multiply per element.
       f32x4_t sacc[2][2], dpacc[2][2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a) {
+        const float4 d4 = *reinterpret_cast<const float4*>(ddl + 32 * qs + 16 * a + 4 * lg);
+        const f32x4_t negd = {-d4.x, -d4.y, -d4.z, -d4.w};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) sacc[a][b] = dpacc[a][b] = f32x4_t{};
+        for (int b = 0; b < 2; ++b) {
+          sacc[a][b] = f32x4_t{};
+          dpacc[a][b] = negd;
+        }
+      }
       // operand reads run two (s, q16) pairs ahead of their MFMAs (one wave
       // per SIMD: nothing else hides the LDS latency); the scheduling
       // barrier keeps the compiler from sinking the reads back to their use
@@ -289,16 +298,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
 #pragma unroll
       for (int q16 = 0; q16 < 2; ++q16) {
         const float4 l4 = *reinterpret_cast<const float4*>(lsl + 32 * qs + 16 * q16 + 4 * lg);
-        const float4 d4 = *reinterpret_cast<const float4*>(ddl + 32 * qs + 16 * q16 + 4 * lg);
         const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float e = fast_exp2(fmaf(sacc[q16][kh][i], c, -lv[i]));
             sacc[q16][kh][i] = e;
-            dpacc[q16][kh][i] = e * (dpacc[q16][kh][i] - dd[i]);
+            dpacc[q16][kh][i] = e * dpacc[q16][kh][i];
           }
       }
       bf16x8_t pf[2], sf[2];
@@ -486,7 +493,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     // S^T and dP^T blocks (key half kh, query half qh): eight chains
     f32x4_t sacc[2][2], dpacc[2][2];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) sacc[kh][0] = sacc[kh][1] = dpacc[kh][0] = dpacc[kh][1] = f32x4_t{};
+    for (int kh = 0; kh < 2; ++kh) {
+      // dP^T accumulators start at -D of their query (all four registers of
+      // a lane belong to query qlo + 16 qh + li): the MFMAs leave dP - D
+      sacc[kh][0] = sacc[kh][1] = f32x4_t{};
+      dpacc[kh][0] = f32x4_t{-dsq[0], -dsq[0], -dsq[0], -dsq[0]};
+      dpacc[kh][1] = f32x4_t{-dsq[1], -dsq[1], -dsq[1], -dsq[1]};
+    }
     // operand reads run one (s4, kh) pair ahead of their MFMAs
     bf16x8_t ka = lds_frag(kl, roff[0]), va = lds_frag(vl, roff[0]);
 #pragma unroll
@@ -548,7 +561,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e = fast_exp2(fmaf(sacc[kh][qh][i], c, -lse2[qh]));
-          dpacc[kh][qh][i] = e * (dpacc[kh][qh][i] - dsq[qh]);
+          dpacc[kh][qh][i] = e * dpacc[kh][qh][i];
         }
     // dQ^T += K^T.dS^T
     bf16x8_t sf[2];
