@@ -75,11 +75,6 @@ __device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
   lo = __uint_as_float(r[0]);
   hi = __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float max_halves(float x) {
-  float a, b;
-  half_pair(x, a, b);
-  return fmaxf(a, b);
-}
 __device__ __forceinline__ float sum_halves(float x) {
   float a, b;
   half_pair(x, a, b);

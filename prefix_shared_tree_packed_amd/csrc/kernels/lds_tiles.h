@@ -1,6 +1,6 @@
 // Row-major token tiles in LDS for the gfx950 attention kernels: DMA
-// staging (global_load_lds_dwordx4), the chunk swizzle, and the
-// transposing operand reads (ds_read_b64_tr_b16).
+// staging (global_load_lds_dwordx4), the chunk swizzle, and the types of the
+// transposing operand reads (ds_read_b64_tr_b16) that the kernels build on.
 //
 // A tile row holds one token's 128 bf16 (256 bytes); 16-byte chunk c of row
 // r sits at c ^ rsw(r), rsw(r) = 2 (r & 7) + ((r >> 3) & 1).  16 consecutive
@@ -15,7 +15,6 @@ namespace pst {
 
 constexpr int kTileRowB = 256;  // tile row: 128 bf16
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
@@ -75,33 +74,6 @@ __device__ __forceinline__ void dma_tile_s(const char* base, const TileOff<NROWS
     const int n = (NROWS / 16) * wave + i;
     dma16_s(base, o.v[i], __builtin_amdgcn_readfirstlane(dst + n * 1024));
   }
-}
-
-// Lane-constant parts of the transposing reads.  For rows d = D0 + lane % 32
-// (D0 a multiple of 32) and tokens T0 .. T0+15 (T0 a multiple of 16), MFMA
-// slot s of the lane holds token T0 + 8 (s / 4) + 4 half + s % 4 (the order in
-// which the score accumulators feed the B operand).  In each 16-lane group,
-// lane i addresses token T0 + 4 half + i / 4 (+8 for the second read) at
-// columns Dg + 4 (i % 4) .. +3 and receives column Dg + i of four tokens.
-struct TrOff {
-  int lo, hi;
-};
-__device__ __forceinline__ TrOff tr_offsets(int lane) {
-  const int g = lane >> 4, i = lane & 15, half = lane >> 5;
-  const int a = i & 3, j = i >> 2;
-  const int x = 2 * (g & 1) + (a >> 1);  // chunk of column Dg + 4a within the 32-column block
-  const int t0 = 4 * half + j, t1 = t0 + 8;
-  return {t0 * kTileRowB + (((x ^ rsw(t0)) << 4) | ((a & 1) << 3)),
-          t1 * kTileRowB + (((x ^ rsw(t1)) << 4) | ((a & 1) << 3))};
-}
-// A operand of X^T (X a row-major tile) for d-block D0 and token block T0.
-__device__ __forceinline__ bf16x8_t lds_tr_frag(const uint8_t* tile, TrOff o, int T0, int D0) {
-  const uint8_t* base = tile + T0 * kTileRowB;
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + (o.lo ^ (2 * D0))));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + (o.hi ^ (2 * D0))));
-  typedef short i16x8_t __attribute__((ext_vector_type(8)));
-  const i16x8_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8_t, w);
 }
 
 }  // namespace pst
