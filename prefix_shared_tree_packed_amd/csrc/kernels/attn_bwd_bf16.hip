@@ -500,28 +500,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
       dpacc[kh][0] = f32x4_t{-dsq[0], -dsq[0], -dsq[0], -dsq[0]};
       dpacc[kh][1] = f32x4_t{-dsq[1], -dsq[1], -dsq[1], -dsq[1]};
     }
-    // operand reads run one (s4, kh) pair ahead of their MFMAs
-    bf16x8_t ka = lds_frag(kl, roff[0]), va = lds_frag(vl, roff[0]);
+    // operand reads run two (s4, kh) pairs ahead of their MFMAs, held in
+    // place by scheduling barriers
+    auto koffs_f = [&](int f) { return ((f & 1) ? kHalf16 : 0) + roff[f >> 1]; };
+    bf16x8_t kbuf[3], vbuf[3];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
+    for (int f = 0; f < 2; ++f) {
+      kbuf[f] = lds_frag(kl, koffs_f(f));
+      vbuf[f] = lds_frag(vl, koffs_f(f));
+    }
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        bf16x8_t kn = ka, vn = va;
-        if (kh == 0) {
-          kn = lds_frag(kl, kHalf16 + roff[s4]);
-          vn = lds_frag(vl, kHalf16 + roff[s4]);
-        } else if (s4 < 3) {
-          kn = lds_frag(kl, roff[s4 + 1]);
-          vn = lds_frag(vl, roff[s4 + 1]);
-        }
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-          sacc[kh][qh] = mma16(ka, qf[qh][s4], sacc[kh][qh]);
-          dpacc[kh][qh] = mma16(va, df[qh][s4], dpacc[kh][qh]);
-        }
-        ka = kn;
-        va = vn;
+    for (int f = 0; f < 8; ++f) {
+      if (f + 2 < 8) {
+        kbuf[(f + 2) % 3] = lds_frag(kl, koffs_f(f + 2));
+        vbuf[(f + 2) % 3] = lds_frag(vl, koffs_f(f + 2));
       }
+      __builtin_amdgcn_sched_barrier(0);
+      const int s4 = f >> 1, kh = f & 1;
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        sacc[kh][qh] = mma16(kbuf[f % 3], qf[qh][s4], sacc[kh][qh]);
+        dpacc[kh][qh] = mma16(vbuf[f % 3], df[qh][s4], dpacc[kh][qh]);
+      }
+    }
     // Register i of block (kh, qh) is key j = kb + 16 kh + i (kb = k0 + 4 lg)
     // of query q = qlo + 16 qh + li, and j sees q iff j <= q <= se[j].  A
     // partial block first sets its invisible scores to -inf (one branch per
@@ -567,14 +568,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     bf16x8_t sf[2];
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) sf[qh] = pack8(dpacc[0][qh], dpacc[1][qh]);
-    bf16x8_t kt = lds_t16_frag(kl, trv, 0);
+    // transposed K reads two d blocks ahead, held in place the same way
+    bf16x8_t kt[3];
+    kt[0] = lds_t16_frag(kl, trv, 0);
+    kt[1] = lds_t16_frag(kl, trv, 1);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      bf16x8_t ktn = kt;
-      if (db < 7) ktn = lds_t16_frag(kl, trv, db + 1);
-      dqacc[db][0] = mma16(kt, sf[0], dqacc[db][0]);
-      dqacc[db][1] = mma16(kt, sf[1], dqacc[db][1]);
-      kt = ktn;
+      if (db + 2 < 8) kt[(db + 2) % 3] = lds_t16_frag(kl, trv, db + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      dqacc[db][0] = mma16(kt[db % 3], sf[0], dqacc[db][0]);
+      dqacc[db][1] = mma16(kt[db % 3], sf[1], dqacc[db][1]);
     }
   };
 

@@ -25,9 +25,9 @@
 //    arithmetic (the per-lane 64-bit form cost ~10 % of the kernel's time,
 //    VALU issue and registers).  48 KB of LDS and at most 168 VGPRs let
 //    three workgroups share a CU.
-//  * LDS operand reads run one fragment ahead of the MFMAs that use them
-//    (each MFMA pair waits for the read issued one pair earlier, not for
-//    the one just issued).
+//  * LDS operand reads run ahead of the MFMAs that use them: K one
+//    fragment, V^T two d blocks (held in place by a scheduling barrier,
+//    since the compiler otherwise sinks loads back to their use).
 //  * K rows are the A operand of S^T = K.Q^T as they stand (one 16-byte read
 //    per operand, shared by the two 16-query halves); the V^T operands of
 //    O^T += V^T.P^T come from the same row-major V tile through two
@@ -367,14 +367,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
       }
 
       // O^T += V^T.P^T: sixteen independent blocks
-      bf16x8_t vf = lds_vt_frag(vcur, trv, 0);
+      // V^T reads two d blocks ahead of their MFMAs; the scheduling barrier
+      // keeps the compiler from sinking them back next to their use
+      bf16x8_t vb[3];
+      vb[0] = lds_vt_frag(vcur, trv, 0);
+      vb[1] = lds_vt_frag(vcur, trv, 1);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        bf16x8_t vn = vf;
-        if (db < 7) vn = lds_vt_frag(vcur, trv, db + 1);
-        oacc[db][0] = mma16(vf, pf[0], oacc[db][0]);
-        oacc[db][1] = mma16(vf, pf[1], oacc[db][1]);
-        vf = vn;
+        if (db + 2 < 8) vb[(db + 2) % 3] = lds_vt_frag(vcur, trv, db + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[db][0] = mma16(vb[db % 3], pf[0], oacc[db][0]);
+        oacc[db][1] = mma16(vb[db % 3], pf[1], oacc[db][1]);
       }
     }
   };
