@@ -384,10 +384,13 @@ constexpr int kQBuf = kQStep * kRowB;  // 8 KB
 constexpr int kQStV = kQBuf, kQStSe = 2 * kQBuf;
 constexpr int kQStageB = 2 * kQBuf + 4 * kQStep;
 
-// UNIT = false: a workgroup is one 128-query block of one head; UNIT =
-// true: one 32-query unit of four heads of one key/value group (one wave per
-// head), walking the unit's non-empty 32x32 blocks.
-template <bool UNIT>
+// A unit workgroup is one 32-query unit of four heads of one key/value group
+// (one wave per head), walking the unit's non-empty 32x32 blocks; a block
+// workgroup is one 128-query block of one head.  MODE 0: blocks only; 1:
+// units only (heads per group a multiple of four); 2: mixed, for a group
+// size G = 4 m + r: units for the group's first 4 m heads, blocks for its
+// last r (as the forward).
+template <int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
@@ -403,13 +406,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   const int lane = tid % kWave;
   const int li = lane % 16;  // query column of the 16x16 blocks
   const int lg = lane / 16;  // 16-lane group: keys 4 lg .. 4 lg + 3 of each block
-  int g, h, qlo, n_steps;
+  // work ids run group by group (each XCD keeps one group's K/V in its L2):
+  // first the group's units, then its 128-query blocks
+  const int G4 = MODE == 0 ? 0 : G / 4 * 4;  // heads of each group served by units
+  const int GR = G - G4;                     // heads served by 128-query blocks
+  const int per_unit = G4 / 4;               // unit workgroups per unit and group
+  const int u_g = per_unit * (tr.Np / 32);
+  const int per_g = u_g + GR * tr.nb;
+  const int g = logical / per_g;
+  const int rem = logical - g * per_g;
+  const bool UNIT = MODE == 1 || (MODE == 2 && rem < u_g);
+  int h, qlo, n_steps;
   cint32* steps;
-  if constexpr (UNIT) {
-    const int per_unit = G / 4;  // workgroups per unit and group
-    const int per_g = per_unit * (tr.Np / 32);
-    g = logical / per_g;
-    const int rem = logical - g * per_g;
+  if (UNIT) {
     const int rank = rem / per_unit;
     h = g * G + (rem - rank * per_unit) * 4 + wave;
     const int u = cst(tr.unit_order)[rank];
@@ -417,11 +426,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     steps = cst(tr.unit_steps) + cst(tr.unit_ptr)[u];
     n_steps = cst(tr.unit_ptr)[u + 1] - cst(tr.unit_ptr)[u];
   } else {
-    const int per_g = G * tr.nb;
-    g = logical / per_g;
-    const int rem = logical - g * per_g;
-    const int rank = rem / G;
-    h = g * G + (rem - rank * G);
+    const int rb = rem - u_g;
+    const int rank = rb / GR;
+    h = g * G + G4 + (rb - rank * GR);
     const int qb = cst(tr.fwd_order)[rank];
     qlo = qb * kTile + wave * 32;
     // the query block's non-empty 32-key columns (scalar metadata reads)
@@ -635,19 +642,24 @@ hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v
                      static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), tr, hq, hkv, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dQ in 32-query units of four heads when the group size is a multiple
-  // of four, as the forward
-  if ((hq / hkv) % 4 == 0)
-    hipLaunchKernelGGL(bwd_dq_bf16<true>, dim3(static_cast<unsigned>(tr.Np / 32) * (hq / 4)),
-                       dim3(256), 0, stream, static_cast<const bf16_t*>(q),
+  // dQ in 32-query units of four heads for as many heads of each group as a
+  // multiple of four covers, 128-query blocks of one head for the rest, as
+  // the forward
+  const unsigned G = static_cast<unsigned>(hq / hkv), G4 = G / 4 * 4, GR = G - G4;
+  const dim3 grid(static_cast<unsigned>(hkv) *
+                  ((G4 / 4) * static_cast<unsigned>(tr.Np / 32) + GR * static_cast<unsigned>(tr.nb)));
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, static_cast<const bf16_t*>(q),
                        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
                        static_cast<const bf16_t*>(dout), lse, dsum, static_cast<bf16_t*>(dq), tr, hq,
                        hkv, c, scale);
+  };
+  if (GR == 0)
+    launch(bwd_dq_bf16<1>);
+  else if (G4 > 0)
+    launch(bwd_dq_bf16<2>);
   else
-    hipLaunchKernelGGL(bwd_dq_bf16<false>, dim3(static_cast<unsigned>(tr.nb) * hq), dim3(256), 0,
-                       stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum,
-                       static_cast<bf16_t*>(dq), tr, hq, hkv, c, scale);
+    launch(bwd_dq_bf16<0>);
   return hipGetLastError();
 }
 

@@ -140,8 +140,12 @@ def test_bwd_worked_example(gpu_lib):
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("f32", 4, 2, 64), ("bf16", 8, 2, 128),
-                                             ("bf16", 5, 1, 64), ("bf16", 6, 6, 128)])
+                                             ("bf16", 5, 1, 64), ("bf16", 6, 6, 128),
+                                             ("bf16", 10, 2, 128), ("bf16", 12, 2, 128),
+                                             ("bf16", 6, 2, 128)])
 def test_bwd_several_tiles(gpu_lib, dtype, hq, hkv, d):
+    """Group sizes 4 (dQ in units), 1 and 3 (blocks only), 5 and 6 (units
+    for four heads of each group, blocks for the rest)."""
     rng = np.random.default_rng(hq * 13 + d)
     seqs = prompt_groups(rng, 3, 150, 3, 20, 260)
     _bwd_full(gpu_lib, seqs, 1024, hq, hkv, d, dtype, 40 + hq)
