@@ -6,12 +6,17 @@
 //
 //  * Every tile reaches LDS row-major (token rows of 256 bytes) by
 //    global_load_lds_dwordx4 (no VGPRs, no VALU) through three-stage rings,
-//    issued from inline assembly so that only the kernels' own waits gate
-//    the prefetch: Q and dO in 64-query steps for dK/dV (one workgroup per
-//    CU), K and V in 32-key steps for dQ (two workgroups per CU).
+//    issued from inline assembly with the step's base address in SGPRs and
+//    lane offsets fixed for the kernel, so that only the kernels' own waits
+//    gate the prefetch: Q and dO in 64-query steps for dK/dV (one workgroup
+//    per CU), K and V in 32-key steps for dQ (two workgroups per CU; in
+//    32-query units of four heads for the largest multiple of four of each
+//    head group, in 128-query blocks for the rest, as the forward).
 //  * Both passes use 16x16x32 MFMAs throughout, so every wave has eight
 //    independent S / dP chains and sixteen independent dK / dV (or dQ)
-//    blocks in flight.
+//    blocks in flight.  LDS operand reads run two fragments ahead of their
+//    MFMAs, held there by scheduling barriers.  The dP accumulators start
+//    at -D, so the MFMAs leave dP - D.
 //  * Products that contract over tokens need the tile transposed (dV^T +=
 //    dO^T.P, dK^T += Q^T.dS, dQ^T += K^T.dS^T).  Their A operands come from
 //    the same row-major tile through ds_read_b64_tr_b16: two transposing
@@ -21,9 +26,11 @@
 //    ((r >> 3) & 1): 16 consecutive rows reading one chunk each hit 16
 //    distinct positions, and a transposing read (4 aligned rows x 2 adjacent
 //    chunks per 16 lanes) hits 8 distinct positions: no bank conflicts.
-//  * Work per (wave, 32x32 sub-block) is skipped when no pair is visible and
-//    masked element by element only when some are: (unsigned)(i - j) <=
-//    se[j] - j.
+//  * Work per (wave, 32x32 sub-block) is skipped when no pair is visible; a
+//    partially visible one first sets its invisible scores to -inf in one
+//    pass under one branch (dK/dV: (unsigned)(i - j) <= se[j] - j; dQ, as
+//    the forward: i <= se[j] alone off the diagonal, j <= i as a second pass
+//    on it), so fully visible sub-blocks pay no mask.
 //  * P is rounded to bf16 before the dV product and dS before the dK and dQ
 //    products; accumulation is fp32.
 #include "launch.h"

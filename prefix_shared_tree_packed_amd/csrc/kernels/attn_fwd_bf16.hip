@@ -1,10 +1,10 @@
 // Tree attention forward pass, bf16 with head_dim 128: the performance path
 // on gfx950.  Same mathematics as attn_fwd.hip.  A workgroup is four waves of
-// 32 query rows: when the query heads per key/value head are a multiple of
-// four, the four waves are four heads of one group on the same 32 queries
-// (a "unit": every wave has work in every step, and each staged K/V tile
-// serves four heads); otherwise they are the four 32-row slices of one
-// 128-query block of one head.  How every step is fed:
+// 32 query rows: for the largest multiple of four of each key/value group's
+// query heads, the four waves are four heads of the group on the same 32
+// queries (a "unit": every wave has work in every step, and each staged K/V
+// tile serves four heads); for the remaining heads they are the four 32-row
+// slices of one 128-query block of one head.  How every step is fed:
 //
 //  * All products use v_mfma_f32_16x16x32_bf16.  A wave's 32 queries x 32
 //    keys of scores are four 16x16 blocks, accumulated as four independent
@@ -13,7 +13,8 @@
 //    at a fraction of the matrix core's rate), and O^T is sixteen
 //    independent 16x16 blocks.  S^T = K.Q^T puts one query in each lane
 //    column: a lane holds four keys of each block, so a query's row
-//    reductions span the four 16-lane groups (two permlane swaps).
+//    reductions span the four 16-lane groups (three permlane swaps serve
+//    both 16-query halves at once).
 //  * The unit's non-empty 32x32 blocks (or the block's non-empty 32-key
 //    columns, dropping columns no wave sees), listed by the host, are walked
 //    through a three-stage LDS ring: while the waves compute one step, the K and V rows
@@ -23,8 +24,9 @@
 //    Each copy takes the step's base address in SGPRs and a lane offset
 //    fixed for the whole kernel, so staging costs no per-lane address
 //    arithmetic (the per-lane 64-bit form cost ~10 % of the kernel's time,
-//    VALU issue and registers).  48 KB of LDS and at most 168 VGPRs let
-//    three workgroups share a CU.
+//    VALU issue and registers); in units they are spread over the S^T
+//    MFMAs.  48 KB of LDS and at most 168 VGPRs let three workgroups share
+//    a CU.
 //  * LDS operand reads run ahead of the MFMAs that use them: K one
 //    fragment, V^T two d blocks (held in place by a scheduling barrier,
 //    since the compiler otherwise sinks loads back to their use).
@@ -35,13 +37,15 @@
 //    which the score registers feed P^T.
 //  * The mask is evaluated per (wave, 32-key block): a block whose keys no
 //    query of the wave sees is skipped (no MFMA, no exp), a block every query
-//    sees runs unmasked, and only the rest pay the per-element test
-//    (unsigned)(i - j) <= se[j] - j, three VALU ops.
+//    sees runs unmasked, and only the rest pay a per-element test under one
+//    branch: i <= se[j] alone off the diagonal (one compare), plus j <= i as
+//    a second pass on the diagonal block.
 //  * Scores stay unscaled; the softmax scale is folded into the exponent's
 //    FMA, and the running max is refreshed lazily: O and the row sums are
 //    rescaled only when a row's max grows by more than 2^8, so exponentials
 //    stay below 256 and most steps skip the rescale.  Row sums stay per lane
-//    (each lane's own keys) until the end.
+//    (each lane's own keys) until the end, and are taken on the bf16
+//    probabilities that O accumulates, two per v_dot2 against (1, 1).
 #include "launch.h"
 #include "lds_tiles.h"
 #include "mfma.h"
