@@ -7,7 +7,7 @@
 // 0 hidden) or an additive float32 / bf16 mask (0 visible, -inf hidden).
 //
 // Each thread owns one 16-byte chunk of columns and keeps their subtree
-// ends in registers; a workgroup walks kRowsPerWg rows, writing every chunk
+// ends in registers; a workgroup walks kRowsPerWg (4) rows, writing every chunk
 // once with a non-temporal store.  Write-bound: Np * Np * element bytes.
 #include "launch.h"
 
@@ -15,7 +15,7 @@ namespace pst {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerWg = 32;
+constexpr int kRowsPerWg = 4;  // small workgroups: enough waves in flight to saturate writes
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
