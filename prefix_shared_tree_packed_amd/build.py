@@ -31,6 +31,12 @@ HIP_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+# Per-source additions.  The bf16 forward schedules best with the iterative
+# ILP strategy (measured +2 % on five query heads per key/value head, no loss
+# elsewhere); the backward loses ~1 % with it and keeps the default.
+FILE_FLAGS = {
+    "kernels/attn_fwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 HIP_SOURCES = [
     "capi.cpp",
@@ -73,7 +79,8 @@ def build(verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        jobs.append([hipcc, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src),
+                     "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
