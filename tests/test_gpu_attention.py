@@ -256,3 +256,22 @@ def test_forest_meta_matches_per_tree(gpu_lib, hq):
         fmeta.destroy()
     finally:
         case.close()
+
+def _degenerate_inputs():
+    """Single-token sequences (two of them identical, one a prefix of longer
+    sequences), and trees of exactly 128 tokens (no pad rows) and of 129
+    (one real row in a second block, 127 pad rows)."""
+    rng = np.random.default_rng(77)
+    singles = [np.array([5], np.int32), np.array([5], np.int32), np.array([9], np.int32),
+               np.array([3], np.int32), np.array([3, 4, 5, 6], np.int32), np.array([3, 4], np.int32)]
+    return [(singles, 128),
+            ([rng.integers(0, 500, 128).astype(np.int32)], 128),
+            ([rng.integers(0, 500, 129).astype(np.int32)], 256)]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("f32", 4, 2, 64), ("bf16", 8, 2, 128),
+                                             ("bf16", 10, 2, 128)])
+def test_fwd_bwd_degenerate_inputs(gpu_lib, dtype, hq, hkv, d):
+    for i, (seqs, cap) in enumerate(_degenerate_inputs()):
+        _fwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, 90 + i)
+        _bwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, 95 + i)

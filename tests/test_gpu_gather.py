@@ -151,3 +151,15 @@ def test_gather_masked_vocabulary(gpu_lib):
                 assert_close(enth, rent, dtype, "entropy[masked]", **_tol(dtype))
     finally:
         case.close()
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gather_degenerate_inputs(gpu_lib, dtype):
+    """Single-token sequences (logprob 0 at the only position; two identical
+    ones and one that is a prefix of longer sequences), and trees of exactly
+    128 and 129 tokens."""
+    rng = np.random.default_rng(78)
+    singles = [np.array([5], np.int32), np.array([5], np.int32), np.array([9], np.int32),
+               np.array([3], np.int32), np.array([3, 4, 5, 6], np.int32), np.array([3, 4], np.int32)]
+    _run(gpu_lib, singles, 128, 64, dtype, 11)
+    _run(gpu_lib, [rng.integers(0, 500, 128).astype(np.int32)], 128, 512, dtype, 12)
+    _run(gpu_lib, [rng.integers(0, 500, 129).astype(np.int32)], 256, 512, dtype, 13)
