@@ -132,3 +132,25 @@ def test_pad_to_maximum_path(gpu_lib, dtype, hq, hkv, d):
             assert_close(host(ent), rent, "f32", "entropy", rtol=0 if tol else None, atol=tol)
     finally:
         case.close()
+
+def _degenerate_inputs():
+    """Single-token sequences (two identical, one a prefix of longer ones),
+    and trees of exactly 128 and of 129 tokens."""
+    rng = np.random.default_rng(79)
+    singles = [np.array([5], np.int32), np.array([5], np.int32), np.array([9], np.int32),
+               np.array([3], np.int32), np.array([3, 4, 5, 6], np.int32), np.array([3, 4], np.int32)]
+    return [(singles, 128), ([rng.integers(0, 500, 128).astype(np.int32)], 128),
+            ([rng.integers(0, 500, 129).astype(np.int32)], 256)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_mask_degenerate_inputs(gpu_lib, fmt):
+    for seqs, cap in _degenerate_inputs():
+        case = Case(seqs, cap)
+        try:
+            for t, tree in enumerate(case.ref.trees):
+                M = oracle.dense_mask(tree)
+                got = gpu_lib.tree_dense_mask(case.metas[t], fmt)
+                _check_mask(got, M, fmt, f"tree {t} ({len(seqs)} sequences, cap {cap})")
+        finally:
+            case.close()

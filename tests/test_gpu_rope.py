@@ -115,3 +115,18 @@ def test_rope_rejects_bad_head_dim(gpu_lib):
         assert e.value.name == "PST_ESHAPE"
     finally:
         case.close()
+
+def _degenerate_inputs():
+    """Single-token sequences (two identical, one a prefix of longer ones),
+    and trees of exactly 128 and of 129 tokens."""
+    rng = np.random.default_rng(79)
+    singles = [np.array([5], np.int32), np.array([5], np.int32), np.array([9], np.int32),
+               np.array([3], np.int32), np.array([3, 4, 5, 6], np.int32), np.array([3, 4], np.int32)]
+    return [(singles, 128), ([rng.integers(0, 500, 128).astype(np.int32)], 128),
+            ([rng.integers(0, 500, 129).astype(np.int32)], 256)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope_degenerate_inputs(gpu_lib, dtype):
+    for i, (seqs, cap) in enumerate(_degenerate_inputs()):
+        _run(gpu_lib, seqs, cap, 8, 128, dtype, 70 + i)
