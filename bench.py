@@ -348,6 +348,7 @@ def main():
         "causal_pairs": stats["causal_pairs"],
         "tiles": stats["n_tiles"],
         "tile_utilisation": pairs / (stats["n_tiles"] * 128 * 128),
+        "block_utilisation": pairs / (blocks32(shape_forest) * 32 * 32),
         "host_build_ms": host_build_ms,
         "kernels": kernels,
         "roofline": roof,
@@ -397,6 +398,18 @@ def time_dense_mask(pst, torch, forest, sizes, stream, steps):
         m.destroy()
     del buf
     return t, sum(s["n_padded"] ** 2 + 4 * s["n_padded"] for s in sizes)
+
+
+def blocks32(forest):
+    """Non-empty 32x32 blocks over all trees: the granularity at which the
+    attention kernels execute MFMAs (2-bit classes packed in each 128-tile)."""
+    import numpy as np
+
+    n = 0
+    for t in range(forest.n_trees):
+        cls = forest.export(t)["q_cls"].view(np.uint32)
+        n += sum(int(np.count_nonzero((cls >> (2 * i)) & 3)) for i in range(16))
+    return n
 
 
 def host_packing(pst, w, forest, ranks=8, reps=5):
