@@ -36,6 +36,14 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA peaks of MI355X
 PEAK_HBM_GBPS = 8000.0
 
 
+def attn_flops(pairs, hq, head_dim):
+    """Algorithmic attention FLOPs: 4 d per visible (query, key) pair and
+    query head forward (score and P.V products), 2.5 times that backward
+    (dV, dP, dQ, dK and the recomputed scores)."""
+    fwd = 4 * head_dim * hq * pairs
+    return dict(fwd=fwd, bwd=2.5 * fwd, fwd_bwd=3.5 * fwd)
+
+
 KDIR = os.path.join(ROOT, "prefix_shared_tree_packed_amd", "csrc", "kernels")
 
 
@@ -265,8 +273,9 @@ def main():
 
     K = args.steps
     pairs = stats["n_pairs"]
-    fwd_flops = 4.0 * d * hq * pairs
-    bwd_flops = 2.5 * fwd_flops if w.bwd else 0.0
+    flops = attn_flops(pairs, hq, d)
+    fwd_flops = float(flops["fwd"])
+    bwd_flops = float(flops["bwd"]) if w.bwd else 0.0
     fwd_t = sum(fwd_ms) / K * 1e-3           # seconds of forward kernels per step
     bwd_t = sum(bwd_ms) / K * 1e-3 if w.bwd else 0.0  # (no kernel between the events otherwise)
     gat_t = sum(gat_ms) / K * 1e-3

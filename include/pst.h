@@ -267,8 +267,10 @@ int pst_gather_tree_logprobs_entropy_bwd(const void* logits, int64_t vocab, int3
 /* ---- device: tree-position rotary embedding -------------------------------- */
 
 /* Rotary position embedding of packed tokens, in place, with position =
- * depth in the trie (the position the token has in every sequence through
- * it: TrieNode / "树构建过程" step 4, the position_ids the model receives).
+ * depth in the trie: the position the token has in every sequence through
+ * it, which is what the position_ids that the tree-training page's "Archon
+ * 引擎" section passes to the model alongside the tree metadata hold for a
+ * packed tree.
  * For each row, head and i < head_dim/2, dims i and i + head_dim/2 are
  * rotated by a = pos * theta^(-2i/head_dim) (rotate-half pairing):
  *   y_i = x_i cos a - x_{i+d/2} sin a,   y_{i+d/2} = x_{i+d/2} cos a + x_i sin a

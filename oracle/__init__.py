@@ -26,11 +26,11 @@ from .tree import (  # noqa: F401
     Node, Tree, Forest, build_forest, BLOCK,
 )
 from .attention import (  # noqa: F401
-    ancestors, dense_mask, attn_fwd, attn_bwd, attn_fwd_rows, attn_bwd_rows,
+    ancestors, dense_mask, attn_fwd, attn_bwd, attn_bwd_magnitudes, attn_fwd_rows, attn_bwd_rows,
 )
 from .gather import (  # noqa: F401
     gather_logprobs_entropy, gather_logprobs_entropy_bwd, row_lse_entropy,
 )
-from .accounting import forest_stats  # noqa: F401
+from .accounting import forest_stats, attn_flops  # noqa: F401
 from .rope import rope  # noqa: F401
 from . import packing  # noqa: F401

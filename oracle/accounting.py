@@ -30,5 +30,9 @@ def forest_stats(forest: Forest, seqs=None) -> dict:
 
 
 def attn_flops(pairs: int, hq: int, head_dim: int) -> dict:
+    """Algorithmic FLOPs of tree attention over `pairs` visible (query, key)
+    pairs per query head: forward 2 d for the score and 2 d for the P.V
+    product per pair and head; backward 2.5 times that (dV, dP, dQ and dK
+    products plus the recomputed scores).  fwd_bwd is their sum."""
     fwd = 4 * head_dim * hq * pairs
     return dict(fwd=fwd, bwd=2.5 * fwd, fwd_bwd=3.5 * fwd)

@@ -107,6 +107,41 @@ def attn_bwd(tree: Tree, q, k, v, dout, scale=None, mask=None):
     return dq, dk, dv
 
 
+def attn_bwd_magnitudes(tree: Tree, q, k, v, dout, scale=None, mask=None):
+    """The backward of attn_bwd with every term taken by absolute value:
+
+        mdQ[i]  = s * sum_j P_ij (|dP_ij| + |D_i|) |K_j|
+        mdK[j]  = s * sum_i P_ij (|dP_ij| + |D_i|) |Q_i|
+        mdV[j]  = sum_i P_ij |dO_i|
+
+    (dP_ij = dO_i . V_j, D_i = dO_i . O_i; P >= 0 needs no bars).  Each entry
+    bounds the size of the terms that the gradient entry sums, so
+    |dQ| <= mdQ and so on, and a rounding error in any of those terms is a
+    small multiple of the unit roundoff times this magnitude.  dS = P (dP - D)
+    cancels: where dP_ij and D_i nearly agree (a token that sees only itself
+    has dP = D exactly) the gradient is far smaller than its terms, and only
+    the magnitude says how large the rounding of a computed value may be.
+    float64, same shapes as attn_bwd."""
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    Np, hq, d = q.shape
+    G = _group(hq, k.shape[1])
+    s = _scale(d, scale)
+    M = dense_mask(tree) if mask is None else mask
+    mq, mk, mv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in range(hq):
+        g = h // G
+        S = np.where(M, s * (q[:, h, :] @ k[:, g, :].T), -np.inf)
+        P = np.exp(S - _logsumexp(S)[:, None])
+        O = P @ v[:, g, :]
+        Drow = (dout[:, h, :] * O).sum(axis=1)
+        dP = dout[:, h, :] @ v[:, g, :].T
+        W = P * (np.abs(dP) + np.abs(Drow)[:, None])
+        mv[:, g, :] += P.T @ np.abs(dout[:, h, :])
+        mq[:, h, :] = s * (W @ np.abs(k[:, g, :]))
+        mk[:, g, :] += s * (W.T @ np.abs(q[:, h, :]))
+    return mq, mk, mv
+
+
 def attn_fwd_rows(tree: Tree, q, k, v, rows: Iterable[int], heads: Iterable[int],
                   scale=None):
     """The forward definition evaluated for selected (row, head) pairs only,
@@ -143,17 +178,24 @@ def attn_bwd_rows(tree: Tree, q, k, v, dout, dq_rows: Iterable[int],
     g, heads = heads_of_group
     f64 = lambda x: np.asarray(x, dtype=np.float64)  # noqa: E731
 
+    anc_of, terms = {}, {}
+
     def row_terms(i, h):
-        anc = ancestors(tree, i)
-        qi, doi = f64(q[i, h, :]), f64(dout[i, h, :])
-        kk, vv = f64(k[anc, g, :]), f64(v[anc, g, :])
-        sc = s * (kk @ qi)
-        p = np.exp(sc - sc.max())
-        p /= p.sum()
-        o = p @ vv
-        dp = vv @ doi
-        ds = p * (dp - doi @ o)
-        return anc, p, ds, qi, doi
+        # each (query, head) is evaluated once, however many requested keys it sees
+        if (i, h) not in terms:
+            if i not in anc_of:
+                anc_of[i] = ancestors(tree, i)
+            anc = anc_of[i]
+            qi, doi = f64(q[i, h, :]), f64(dout[i, h, :])
+            kk, vv = f64(k[anc, g, :]), f64(v[anc, g, :])
+            sc = s * (kk @ qi)
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            o = p @ vv
+            dp = vv @ doi
+            ds = p * (dp - doi @ o)
+            terms[(i, h)] = (anc, p, ds, qi, doi)
+        return terms[(i, h)]
 
     dq = {}
     for i in dq_rows:

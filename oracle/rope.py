@@ -1,10 +1,11 @@
 """Oracle: rotary position embedding of packed tree tokens (test
 infrastructure only).
 
-The tree-training page (TrieNode / 树构建过程) gives every packed token the
-position it has in each sequence that contains it: its depth in the trie,
-exported as `pos`.  That is the position_ids the model receives, so rotary
-embeddings of the packed Q and K use pos = depth.  The rotation is the
+The tree-training page's "Archon 引擎" section passes position_ids to the
+model together with the tree metadata.  For a packed tree the position of a
+token is the one it has in every sequence that contains it: its depth in the
+trie, exported as `pos`.  So rotary embeddings of the packed Q and K use
+pos = depth.  The rotation is the
 standard one (RoFormer), in the rotate-half pairing: for head_dim d and
 i < d/2, dims i and i + d/2 form a pair rotated by the angle
 pos * theta^(-2i/d) (theta = 10000 unless given):

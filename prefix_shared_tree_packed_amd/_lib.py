@@ -9,7 +9,9 @@ import re
 from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpst.so")
+# PST_LIBRARY selects another build of the library (the CPU sanitizer build of
+# the host entry points, for instance); by default the in-tree libpst.so
+LIB_PATH = os.environ.get("PST_LIBRARY") or os.path.join(PKG, "libpst.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "pst.h")
 
 PST_OK = 0
@@ -121,7 +123,11 @@ def load(path: str = LIB_PATH):
         raise RuntimeError(f"{path} is not built; run `python -m prefix_shared_tree_packed_amd.build`")
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGS.items():
-        fn = getattr(lib, name)
+        # a build without the device entry points (the host-only sanitizer
+        # build) leaves them undeclared: calling one raises AttributeError
+        fn = getattr(lib, name, None)
+        if fn is None:
+            continue
         fn.restype = res
         fn.argtypes = args
     _lib = lib

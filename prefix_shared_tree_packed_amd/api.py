@@ -47,10 +47,24 @@ def _ptr_or_null(t):
 
 
 def _dev_tensor(t, name):
+    import torch
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _checked(t, name, shape, dtype):
+    """A caller-supplied buffer: a contiguous device tensor of exactly this
+    shape and dtype (the library sees only its pointer, so a smaller or
+    differently typed buffer would be read or written out of bounds)."""
+    _dev_tensor(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {list(shape)}, got {t.dtype} {list(t.shape)}")
     return t
 
 
@@ -189,13 +203,13 @@ def tree_attn_fwd(q, k, v, meta: TreeMeta, softmax_scale: Optional[float] = None
                          f"do not match a tree of {meta.n_padded} padded rows")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((hq, Np), dtype=torch.float32, device=q.device)
+    code = _dtype_code(q)
+    out = torch.empty_like(q) if out is None else _checked(out, "out", q.shape, q.dtype)
+    lse = (torch.empty((hq, Np), dtype=torch.float32, device=q.device) if lse is None
+           else _checked(lse, "lse", (hq, Np), torch.float32))
     check(_lib.load().pst_tree_attn_fwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), _dev_tensor(out, "out").data_ptr(),
-        _dev_tensor(lse, "lse").data_ptr(), meta._h, hq, hkv, d, _dtype_code(q),
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        lse.data_ptr(), meta._h, hq, hkv, d, code,
         float(softmax_scale or 0.0), c_void_p(_stream_ptr(stream))))
     return out, lse
 
@@ -219,18 +233,23 @@ def tree_attn_bwd(q, k, v, o, lse, dout, meta: TreeMeta, softmax_scale: Optional
     if (k.shape != (Np, hkv, d) or v.shape != k.shape or o.shape != q.shape
             or dout.shape != q.shape or tuple(lse.shape) != (hq, Np) or Np != meta.n_padded):
         raise ValueError("shape mismatch in tree_attn_bwd arguments")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise TypeError("q, k, v, o, dout must share a dtype")
+    if lse.dtype != torch.float32:
+        raise ValueError(f"lse must be float32, got {lse.dtype}")
+    code = _dtype_code(q)
+    dq = torch.empty_like(q) if dq is None else _checked(dq, "dq", q.shape, q.dtype)
+    dk = torch.empty_like(k) if dk is None else _checked(dk, "dk", k.shape, k.dtype)
+    dv = torch.empty_like(v) if dv is None else _checked(dv, "dv", v.shape, v.dtype)
     nbytes = tree_attn_bwd_workspace_bytes(meta, hq, hkv, d,
                                            "bf16" if q.dtype == torch.bfloat16 else "f32")
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _dev_tensor(workspace, "workspace")
     check(_lib.load().pst_tree_attn_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-        _dev_tensor(dq, "dq").data_ptr(), _dev_tensor(dk, "dk").data_ptr(),
-        _dev_tensor(dv, "dv").data_ptr(), _dev_tensor(workspace, "workspace").data_ptr(),
-        workspace.numel() * workspace.element_size(), meta._h, hq, hkv, d, _dtype_code(q),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), meta._h, hq, hkv, d, code,
         float(softmax_scale or 0.0), c_void_p(_stream_ptr(stream))))
     return dq, dk, dv
 
@@ -239,10 +258,7 @@ def _row_stats(t, meta, name="row_stats"):
     import torch
     if t is None:
         return None
-    _dev_tensor(t, name)
-    if t.dtype != torch.float32 or tuple(t.shape) != (meta.n_padded, 2):
-        raise ValueError(f"{name} must be float32 [{meta.n_padded}, 2]")
-    return t
+    return _checked(t, name, (meta.n_padded, 2), torch.float32)
 
 
 def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=None,
@@ -255,13 +271,14 @@ def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=
     if logits.dim() != 2 or logits.shape[0] != meta.n_padded:
         raise ValueError(f"logits must be [{meta.n_padded}, V], got {tuple(logits.shape)}")
     n = meta.n_out
-    if logprobs is None:
-        logprobs = torch.empty(n, dtype=torch.float32, device=logits.device)
-    if entropy is None:
-        entropy = torch.empty(n, dtype=torch.float32, device=logits.device)
+    code = _dtype_code(logits)
+    logprobs = (torch.empty(n, dtype=torch.float32, device=logits.device) if logprobs is None
+                else _checked(logprobs, "logprobs", (n,), torch.float32))
+    entropy = (torch.empty(n, dtype=torch.float32, device=logits.device) if entropy is None
+               else _checked(entropy, "entropy", (n,), torch.float32))
     check(_lib.load().pst_gather_tree_logprobs_entropy(
-        logits.data_ptr(), int(logits.shape[1]), _dtype_code(logits), meta._h,
-        _dev_tensor(logprobs, "logprobs").data_ptr(), _dev_tensor(entropy, "entropy").data_ptr(),
+        logits.data_ptr(), int(logits.shape[1]), code, meta._h,
+        logprobs.data_ptr(), entropy.data_ptr(),
         c_void_p(_ptr_or_null(_row_stats(row_stats, meta))), c_void_p(_stream_ptr(stream))))
     return logprobs, entropy
 
@@ -276,18 +293,15 @@ def gather_tree_logprobs_entropy_bwd(logits, meta: TreeMeta, dlogprobs, dentropy
     if logits.dim() != 2 or logits.shape[0] != meta.n_padded:
         raise ValueError(f"logits must be [{meta.n_padded}, V], got {tuple(logits.shape)}")
     for t, name in ((dlogprobs, "dlogprobs"), (dentropy, "dentropy")):
-        _dev_tensor(t, name)
-        if t.dtype != torch.float32 or t.numel() != meta.n_out:
-            raise ValueError(f"{name} must be float32 [{meta.n_out}]")
-    if dlogits is None:
-        dlogits = torch.empty_like(logits)
-    elif dlogits.shape != logits.shape or dlogits.dtype != logits.dtype:
-        raise ValueError("dlogits must match logits in shape and dtype")
+        _checked(t, name, (meta.n_out,), torch.float32)
+    code = _dtype_code(logits)
+    dlogits = (torch.empty_like(logits) if dlogits is None
+               else _checked(dlogits, "dlogits", logits.shape, logits.dtype))
     check(_lib.load().pst_gather_tree_logprobs_entropy_bwd(
-        logits.data_ptr(), int(logits.shape[1]), _dtype_code(logits), meta._h,
+        logits.data_ptr(), int(logits.shape[1]), code, meta._h,
         dlogprobs.data_ptr(), dentropy.data_ptr(),
         c_void_p(_ptr_or_null(_row_stats(row_stats, meta))),
-        _dev_tensor(dlogits, "dlogits").data_ptr(), c_void_p(_stream_ptr(stream))))
+        dlogits.data_ptr(), c_void_p(_stream_ptr(stream))))
     return dlogits
 
 

@@ -48,7 +48,12 @@ HIP_SOURCES = [
     "kernels/rope.hip",
     "kernels/mask.hip",
 ]
-CXX_SOURCES = ["host/forest.cpp", "host/packing.cpp"]
+CXX_SOURCES = ["capi_host.cpp", "host/forest.cpp", "host/packing.cpp"]
+# the CPU-only sanitizer build of the host entry points (no HIP code in it)
+SAN_LIB = os.path.join(BUILD, "sanitize", "libpst_host_san.so")
+SAN_FLAGS = ["-O1", "-g", "-std=c++17", "-fPIC", "-Wall", "-fno-omit-frame-pointer",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
 def _hipcc() -> str:
@@ -94,5 +99,21 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The host-only entry points (builder, forest accessors, packing, error
+    status) compiled by g++ with AddressSanitizer and UndefinedBehaviorSanitizer
+    into a CPU library of their own (no device entry points); returns its
+    path.  Loading it into Python needs libasan preloaded."""
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    srcs = [os.path.join(CSRC, s) for s in CXX_SOURCES]
+    tmp = SAN_LIB + ".tmp"
+    _run(["g++", *SAN_FLAGS, "-shared", *srcs, "-o", tmp], verbose)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

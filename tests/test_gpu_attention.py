@@ -104,16 +104,8 @@ def test_fwd_grpo_sampled(gpu_lib):
     _fwd_sampled(gpu_lib, "grpo")
 
 
-def test_fwd_bimodal_sampled(gpu_lib):
-    _fwd_sampled(gpu_lib, "bimodal", n_trees=3)
-
-
 def test_fwd_long_sampled(gpu_lib):
     _fwd_sampled(gpu_lib, "long", n_rows=24)
-
-
-def test_fwd_long_control_sampled(gpu_lib):
-    _fwd_sampled(gpu_lib, "long_control", n_rows=16, n_trees=2)
 
 
 # ---------------------------------------------------------------- backward
@@ -126,10 +118,12 @@ def _bwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, seed):
             q, k, v, do = attn_inputs(tree.n_padded, hq, hkv, d, dtype, seed + t, with_dout=True)
             o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[t])
             dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[t])
-            rdq, rdk, rdv = oracle.attn_bwd(tree, host(q), host(k), host(v), host(do))
-            assert_close(host(dq), rdq, dtype, "dQ", grad=True)
-            assert_close(host(dk), rdk, dtype, "dK", grad=True)
-            assert_close(host(dv), rdv, dtype, "dV", grad=True)
+            args = (tree, host(q), host(k), host(v), host(do))
+            rdq, rdk, rdv = oracle.attn_bwd(*args)
+            mdq, mdk, mdv = oracle.attn_bwd_magnitudes(*args) if dtype == "f32" else (None,) * 3
+            assert_close(host(dq), rdq, dtype, "dQ", grad=True, mag=mdq)
+            assert_close(host(dk), rdk, dtype, "dK", grad=True, mag=mdk)
+            assert_close(host(dv), rdv, dtype, "dV", grad=True, mag=mdv)
     finally:
         case.close()
 
@@ -173,37 +167,102 @@ def test_bwd_deterministic(gpu_lib):
         case.close()
 
 
-def test_bwd_agentic_sampled(gpu_lib):
-    """Full-size agentic trees: dQ on sampled rows, dK/dV on sampled deep keys
-    (whose visible queries the oracle can enumerate one by one)."""
-    w = get_workload("agentic")
+def _forest_inputs(w, sizes, with_dout=True):
+    """Q, K, V (and dO) of a whole forest, trees back to back, each tree's
+    rows drawn from their own seed (the layout of the forest-level metadata)."""
+    import torch
+    parts = [attn_inputs(s, w.hq, w.hkv, w.head_dim, w.dtype, w.seed * 100 + t, with_dout=with_dout)
+             for t, s in enumerate(sizes)]
+    return [torch.cat([p[n] for p in parts]).contiguous() for n in range(len(parts[0]))]
+
+
+def _fwd_bwd_forest_sampled(gpu_lib, name, n_rows, n_keys, extra_keys=None):
+    """One forest-level forward and backward launch over every tree of a
+    full-size workload; then, tree by tree, O and LSE on sampled rows and
+    heads, dQ on sampled rows, and dK/dV on sampled deep keys (whose visible
+    queries the oracle enumerates one by one) for the first and last
+    key/value groups.  extra_keys(tree) adds keys to check in the last tree
+    (e.g. shared-prompt keys that sum over thousands of queries)."""
+    w = get_workload(name)
     case = Case(w.seqs, w.max_tokens_per_mb)
-    rng = np.random.default_rng(1)
+    rng = np.random.default_rng(w.seed)
+    fmeta = None
     try:
+        sizes = [t.n_padded for t in case.ref.trees]
+        fmeta = gpu_lib.forest_meta_create(case.forest)
+        assert fmeta.n_padded == sum(sizes)
+        print(f"fwd+bwd forest: {name} trees={len(sizes)} Np={sum(sizes)}", flush=True)
+        q, k, v, do = _forest_inputs(w, sizes)
+        o, lse = gpu_lib.tree_attn_fwd(q, k, v, fmeta)
+        dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, fmeta)
+        G = w.hq // w.hkv
+        r0 = 0
         for t, tree in enumerate(case.ref.trees):
-            print(f"bwd sampled: agentic tree={t} Np={tree.n_padded}", flush=True)
-            q, k, v, do = attn_inputs(tree.n_padded, w.hq, w.hkv, w.head_dim, w.dtype,
-                                      w.seed * 100 + t, with_dout=True)
-            o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[t])
-            dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[t])
-            qh, kh, vh, doh = host32(q), host32(k), host32(v), host32(do)
-            dqh, dkh, dvh = host32(dq), host32(dk), host32(dv)
+            sl = slice(r0, r0 + tree.n_padded)
+            r0 += tree.n_padded
+            print(f"  check: {name} tree={t} Np={tree.n_padded}", flush=True)
+            qh, kh, vh, doh = (host32(x[sl]) for x in (q, k, v, do))
+            oh, lh = host32(o[sl]), host32(lse[:, sl])
+            dqh, dkh, dvh = host32(dq[sl]), host32(dk[sl]), host32(dv[sl])
+            rows = sorted(set(rng.integers(0, tree.n_tokens, size=n_rows).tolist())
+                          | {0, tree.n_tokens - 1, tree.n_padded - 1})
+            heads = sorted(set(rng.integers(0, w.hq, size=4).tolist()) | {0, w.hq - 1})
+            ref = oracle.attn_fwd_rows(tree, qh, kh, vh, rows, heads)
+            assert_close(np.array([oh[i, h] for (i, h) in ref]), np.array([x[0] for x in ref.values()]),
+                         w.dtype, f"O[{name} tree {t}]")
+            assert_close(np.array([lh[h, i] for (i, h) in ref]), np.array([x[1] for x in ref.values()]),
+                         w.dtype, f"LSE[{name} tree {t}]")
             se = tree.subtree_end
             deep = [j for j in range(tree.n_tokens) if se[j] - j < 40]
-            keys = sorted(rng.choice(deep, size=8, replace=False).tolist()) + [tree.n_padded - 1]
-            rows = sorted(rng.integers(0, tree.n_tokens, size=8).tolist())
+            keys = sorted(rng.choice(deep, size=min(n_keys, len(deep)), replace=False).tolist())
+            keys.append(tree.n_padded - 1)
+            if extra_keys is not None and t == len(case.ref.trees) - 1:
+                keys = sorted(set(keys) | set(extra_keys(tree)))
+            qrows = sorted(rng.integers(0, tree.n_tokens, size=max(n_rows // 8, 2)).tolist())
             for g in (0, w.hkv - 1):
-                G = w.hq // w.hkv
-                heads = list(range(g * G, (g + 1) * G))
-                rq, rkv = oracle.attn_bwd_rows(tree, qh, kh, vh, doh, rows, keys, (g, heads))
+                hs = list(range(g * G, (g + 1) * G))
+                rq, rkv = oracle.attn_bwd_rows(tree, qh, kh, vh, doh, qrows, keys, (g, hs))
                 assert_close(np.array([dqh[i, h] for (i, h) in rq]), np.array(list(rq.values())),
-                             w.dtype, "dQ[agentic]", grad=True)
+                             w.dtype, f"dQ[{name} tree {t}]", grad=True)
                 assert_close(np.array([dkh[j, gg] for (j, gg) in rkv]),
-                             np.array([x[0] for x in rkv.values()]), w.dtype, "dK[agentic]", grad=True)
+                             np.array([x[0] for x in rkv.values()]), w.dtype,
+                             f"dK[{name} tree {t}]", grad=True)
                 assert_close(np.array([dvh[j, gg] for (j, gg) in rkv]),
-                             np.array([x[1] for x in rkv.values()]), w.dtype, "dV[agentic]", grad=True)
+                             np.array([x[1] for x in rkv.values()]), w.dtype,
+                             f"dV[{name} tree {t}]", grad=True)
     finally:
+        if fmeta is not None:
+            import torch
+            torch.cuda.synchronize()
+            fmeta.destroy()
         case.close()
+
+
+def test_fwd_bwd_agentic_sampled(gpu_lib):
+    """Full-size agentic trees (32 query heads over 8 key/value heads: units
+    only in the forward and dQ)."""
+    _fwd_bwd_forest_sampled(gpu_lib, "agentic", n_rows=32, n_keys=8)
+
+
+def test_fwd_bwd_bimodal_sampled(gpu_lib):
+    """Full-size bimodal forest, all 23 trees in one launch (40 query heads
+    over 8: the forward and dQ run units of four heads plus 128-query blocks
+    for the fifth head of every group); in the last tree also the first key
+    (the prompt's root, seen by every token of the tree) and a later prompt
+    key, whose dK/dV sum over thousands of queries."""
+    _fwd_bwd_forest_sampled(gpu_lib, "bimodal", n_rows=16, n_keys=2,
+                            extra_keys=lambda tree: [0, 100])
+
+
+def test_fwd_bwd_long_sampled(gpu_lib):
+    """Full-size long trees (up to 32 768 tokens, 64 query heads over 8)."""
+    _fwd_bwd_forest_sampled(gpu_lib, "long", n_rows=16, n_keys=3)
+
+
+def test_fwd_bwd_long_control_sampled(gpu_lib):
+    """The no-sharing control of the long workload: every tree is a set of
+    unrelated sequences, so tree attention is varlen causal attention."""
+    _fwd_bwd_forest_sampled(gpu_lib, "long_control", n_rows=12, n_keys=2)
 
 
 def test_invalid_shapes_rejected(gpu_lib):
@@ -275,3 +334,47 @@ def test_fwd_bwd_degenerate_inputs(gpu_lib, dtype, hq, hkv, d):
     for i, (seqs, cap) in enumerate(_degenerate_inputs()):
         _fwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, 90 + i)
         _bwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, 95 + i)
+
+
+def test_output_buffers_checked(gpu_lib):
+    """Caller-supplied outputs of the wrong shape, dtype or device, and
+    inputs of mixed dtypes, are refused in the binding before any launch:
+    the library receives bare pointers and would write past a short buffer."""
+    import torch
+    case = Case(worked_example(), 128)
+    try:
+        m = case.metas[0]
+        q, k, v, do = attn_inputs(128, 4, 2, 128, "bf16", 1, with_dout=True)
+        bad = [
+            dict(out=torch.empty(128, 4, 64, dtype=torch.bfloat16, device="cuda")),
+            dict(out=torch.empty(128, 4, 128, dtype=torch.float32, device="cuda")),
+            dict(lse=torch.empty(4, 128, dtype=torch.bfloat16, device="cuda")),
+            dict(lse=torch.empty(4, 64, dtype=torch.float32, device="cuda")),
+            dict(out=torch.empty(128, 4, 128, dtype=torch.bfloat16)),
+        ]
+        for kw in bad:
+            with pytest.raises(ValueError):
+                gpu_lib.tree_attn_fwd(q, k, v, m, **kw)
+        o, lse = gpu_lib.tree_attn_fwd(q, k, v, m)
+        for kw in (dict(dq=torch.empty_like(k)), dict(dk=torch.empty_like(q)),
+                   dict(dv=torch.empty_like(v, dtype=torch.float32))):
+            with pytest.raises(ValueError):
+                gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, m, **kw)
+        with pytest.raises(TypeError):
+            gpu_lib.tree_attn_bwd(q, k, v, o.float(), lse, do, m)
+        with pytest.raises(ValueError):
+            gpu_lib.tree_attn_bwd(q, k, v, o, lse.to(torch.bfloat16), do, m)
+        logits = torch.zeros(128, 16, dtype=torch.bfloat16, device="cuda")
+        for kw in (dict(logprobs=torch.empty(m.n_out - 1, device="cuda")),
+                   dict(entropy=torch.empty(m.n_out, dtype=torch.float64, device="cuda")),
+                   dict(row_stats=torch.empty(128, 3, device="cuda"))):
+            with pytest.raises(ValueError):
+                gpu_lib.gather_tree_logprobs_entropy(logits, m, **kw)
+        dl = torch.zeros(m.n_out, device="cuda")
+        with pytest.raises(ValueError):
+            gpu_lib.gather_tree_logprobs_entropy_bwd(logits, m, dl, dl,
+                                                     dlogits=torch.empty(128, 8, dtype=torch.bfloat16,
+                                                                         device="cuda"))
+        torch.cuda.synchronize()
+    finally:
+        case.close()

@@ -113,10 +113,12 @@ def test_pad_to_maximum_path(gpu_lib, dtype, hq, hkv, d):
             assert_close(host(o), O, dtype, "O")
             assert_close(host(lse), LSE, dtype, "LSE")
             dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[t])
-            rdq, rdk, rdv = oracle.attn_bwd(tree, host(q), host(k), host(v), host(do))
-            assert_close(host(dq), rdq, dtype, "dQ", grad=True)
-            assert_close(host(dk), rdk, dtype, "dK", grad=True)
-            assert_close(host(dv), rdv, dtype, "dV", grad=True)
+            args = (tree, host(q), host(k), host(v), host(do))
+            rdq, rdk, rdv = oracle.attn_bwd(*args)
+            mdq, mdk, mdv = oracle.attn_bwd_magnitudes(*args) if dtype == "f32" else (None,) * 3
+            assert_close(host(dq), rdq, dtype, "dQ", grad=True, mag=mdq)
+            assert_close(host(dk), rdk, dtype, "dK", grad=True, mag=mdk)
+            assert_close(host(dv), rdv, dtype, "dV", grad=True, mag=mdv)
             qr = q.clone()
             gpu_lib.tree_rope(qr, case.metas[t])
             ref = oracle.rope(host(q), tree.pos)

@@ -191,3 +191,78 @@ def test_bwd_rows_match_dense():
         for (j, gg), (a, b) in gkv.items():
             np.testing.assert_allclose(a, dk[j, gg], atol=1e-12)
             np.testing.assert_allclose(b, dv[j, gg], atol=1e-12)
+
+
+# ------------------------------------------------ gradient term magnitudes
+
+def _magnitudes_brute_force(tree, q, k, v, do, s):
+    """The absolute term sums of every gradient entry, by loops over each
+    query's parent chain (no dense mask, no matrix products): dQ_i sums
+    s P_ij dP_ij K_j and -s P_ij D_i K_j over visible j; dK_j and dV_j sum the
+    matching terms over the queries that see j."""
+    Np, hq, d = q.shape
+    G = hq // k.shape[1]
+    mq, mk, mv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for i in range(Np):
+        anc = oracle.ancestors(tree, i)
+        for h in range(hq):
+            g = h // G
+            sc = np.array([s * float(np.dot(q[i, h], k[j, g])) for j in anc])
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            o = sum(p[n] * v[j, g] for n, j in enumerate(anc))
+            D = float(np.dot(do[i, h], o))
+            for n, j in enumerate(anc):
+                dp = float(np.dot(do[i, h], v[j, g]))
+                for c in range(d):
+                    mq[i, h, c] += abs(s * p[n] * dp * k[j, g, c]) + abs(s * p[n] * D * k[j, g, c])
+                    mk[j, g, c] += abs(s * p[n] * dp * q[i, h, c]) + abs(s * p[n] * D * q[i, h, c])
+                    mv[j, g, c] += abs(p[n] * do[i, h, c])
+    return mq, mk, mv
+
+
+def test_bwd_magnitudes_brute_force():
+    tree = oracle.build_forest(worked_example_edge() + [np.array([1, 2, 9], np.int32)], 128).trees[0]
+    q, k, v, do = _tree_inputs(tree, 4, 2, 3, 12)
+    got = oracle.attn_bwd_magnitudes(tree, q, k, v, do)
+    exp = _magnitudes_brute_force(tree, q, k, v, do, 1 / np.sqrt(3))
+    for a, b in zip(got, exp):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def test_bwd_magnitudes_bound_the_gradients():
+    """|dQ| <= mdQ, |dK| <= mdK, |dV| <= mdV entrywise (triangle inequality);
+    flipping the sign of dO flips the gradients and leaves the magnitudes;
+    with dO >= 0 every dV term is non-negative, so mdV equals dV."""
+    tree = oracle.build_forest(_random_seqs(np.random.default_rng(13)), 256).trees[0]
+    q, k, v, do = _tree_inputs(tree, 4, 2, 8, 14)
+    grads = oracle.attn_bwd(tree, q, k, v, do)
+    mags = oracle.attn_bwd_magnitudes(tree, q, k, v, do)
+    for gr, mg in zip(grads, mags):
+        assert np.all(np.abs(gr) <= mg * (1 + 1e-12) + 1e-15)
+    flipped = oracle.attn_bwd_magnitudes(tree, q, k, v, -do)
+    for a, b in zip(mags, flipped):
+        np.testing.assert_allclose(a, b, rtol=1e-13)
+    pos = np.abs(do)
+    dv = oracle.attn_bwd(tree, q, k, v, pos)[2]
+    np.testing.assert_allclose(oracle.attn_bwd_magnitudes(tree, q, k, v, pos)[2], dv, rtol=1e-12)
+
+
+def test_bwd_magnitudes_single_token():
+    """A token that sees only itself (P = 1, O = V, so dP = D): dQ = dK = 0
+    exactly, while the magnitudes are 2 s |dO.V| |K| and 2 s |dO.V| |Q|
+    (summed over the query heads of the group for K) and |dO| for V."""
+    tree = oracle.build_forest([np.array([7], np.int32)], 128).trees[0]
+    q, k, v, do = _tree_inputs(tree, 2, 1, 4, 15)
+    s = 0.5
+    dq, dk, _ = oracle.attn_bwd(tree, q, k, v, do)
+    mq, mk, mv = oracle.attn_bwd_magnitudes(tree, q, k, v, do)
+    for i in (0, 5, tree.n_padded - 1):         # the real token and two pad rows
+        dp = [abs(float(np.dot(do[i, h], v[i, 0]))) for h in range(2)]
+        np.testing.assert_allclose(dq[i], 0, atol=1e-12)
+        np.testing.assert_allclose(dk[i], 0, atol=1e-12)
+        for h in range(2):
+            np.testing.assert_allclose(mq[i, h], 2 * s * dp[h] * np.abs(k[i, 0]), rtol=1e-12)
+        np.testing.assert_allclose(mk[i, 0], 2 * s * (dp[0] * np.abs(q[i, 0]) + dp[1] * np.abs(q[i, 1])),
+                                   rtol=1e-12)
+        np.testing.assert_allclose(mv[i, 0], np.abs(do[i, 0]) + np.abs(do[i, 1]), rtol=1e-12)
