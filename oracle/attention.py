@@ -108,20 +108,23 @@ def attn_bwd(tree: Tree, q, k, v, dout, scale=None, mask=None):
 
 
 def attn_bwd_magnitudes(tree: Tree, q, k, v, dout, scale=None, mask=None):
-    """The backward of attn_bwd with every term taken by absolute value:
+    """The backward of attn_bwd with every elementary product taken by
+    absolute value, down to the dot products inside dP and D:
 
-        mdQ[i]  = s * sum_j P_ij (|dP_ij| + |D_i|) |K_j|
-        mdK[j]  = s * sum_i P_ij (|dP_ij| + |D_i|) |Q_i|
+        A_ij    = sum_c |dO_ic| |V_jc|              (bounds |dP_ij|, dP = dO.V^T)
+        B_i     = sum_c |dO_ic| sum_j P_ij |V_jc|   (bounds |D_i|, D = rowsum(dO*O))
+        mdQ[i]  = s * sum_j P_ij (A_ij + B_i) |K_j|
+        mdK[j]  = s * sum_i P_ij (A_ij + B_i) |Q_i|
         mdV[j]  = sum_i P_ij |dO_i|
 
-    (dP_ij = dO_i . V_j, D_i = dO_i . O_i; P >= 0 needs no bars).  Each entry
-    bounds the size of the terms that the gradient entry sums, so
-    |dQ| <= mdQ and so on, and a rounding error in any of those terms is a
-    small multiple of the unit roundoff times this magnitude.  dS = P (dP - D)
-    cancels: where dP_ij and D_i nearly agree (a token that sees only itself
-    has dP = D exactly) the gradient is far smaller than its terms, and only
-    the magnitude says how large the rounding of a computed value may be.
-    float64, same shapes as attn_bwd."""
+    (P >= 0 needs no bars).  Each entry is the sum of the sizes of all the
+    products that the gradient entry is built from, so |dQ| <= mdQ and so
+    on, and the rounding of a computed value is at most a small multiple of
+    the unit roundoff times this magnitude.  dS = P (dP - D) cancels (a token
+    that sees only itself has dP = D exactly), and so can the dot products
+    inside dP and D; where they do, the gradient is far smaller than its
+    terms, and only the magnitude says how large a computed value's rounding
+    may be.  float64, same shapes as attn_bwd."""
     q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
     Np, hq, d = q.shape
     G = _group(hq, k.shape[1])
@@ -132,11 +135,11 @@ def attn_bwd_magnitudes(tree: Tree, q, k, v, dout, scale=None, mask=None):
         g = h // G
         S = np.where(M, s * (q[:, h, :] @ k[:, g, :].T), -np.inf)
         P = np.exp(S - _logsumexp(S)[:, None])
-        O = P @ v[:, g, :]
-        Drow = (dout[:, h, :] * O).sum(axis=1)
-        dP = dout[:, h, :] @ v[:, g, :].T
-        W = P * (np.abs(dP) + np.abs(Drow)[:, None])
-        mv[:, g, :] += P.T @ np.abs(dout[:, h, :])
+        adO, aV = np.abs(dout[:, h, :]), np.abs(v[:, g, :])
+        A = adO @ aV.T
+        B = (adO * (P @ aV)).sum(axis=1)
+        W = P * (A + B[:, None])
+        mv[:, g, :] += P.T @ adO
         mq[:, h, :] = s * (W @ np.abs(k[:, g, :]))
         mk[:, g, :] += s * (W.T @ np.abs(q[:, h, :]))
     return mq, mk, mv

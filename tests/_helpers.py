@@ -8,13 +8,16 @@ Tolerances (float outputs; integer outputs are compared bit-exactly):
   bf16 gradients:         |got - ref| <= 2e-2 + 2^-8 |ref|
   logprob/entropy:        |got - ref| <= 1e-3 from bf16 logits, 1e-5 |ref| + 1e-6 from fp32
 
-mag is the entry's own sum of absolute terms (oracle.attn_bwd_magnitudes:
-s sum_j P_ij (|dP_ij| + |D_i|) |K_j| for dQ, and so on): a float32 result
-whose terms are each rounded to a few units of 2^-24 of their size is off by
-at most a small multiple of 2^-24 mag, and mag >= |ref|.  The bound is local
-to the entry: dS = P (dP - D) cancels where dP and D agree (a token that sees
-only itself has dP = D exactly, so its exact dQ and dK are 0), and there the
-computed value is rounding of the terms, which only their magnitude bounds.
+mag is the entry's own sum of the sizes of the products it is built from
+(oracle.attn_bwd_magnitudes: s sum_j P_ij (A_ij + B_i) |K_j| for dQ, with
+A_ij = |dO_i|.|V_j| and B_i = |dO_i|.(sum_j P_ij |V_j|) the absolute sums
+behind dP_ij and D_i, and so on): a float32 result whose products are each
+rounded to a few units of 2^-24 is off by at most a small multiple of
+2^-24 mag, and mag >= |ref|.  The bound is local to the entry: dS = P (dP - D)
+cancels where dP and D agree (a token that sees only itself has dP = D
+exactly, so its exact dQ and dK are 0), and the dot products inside dP and D
+can cancel as well; there the computed value is rounding of the products,
+which only their sizes bound.
 A bf16 gradient is rounded once on output (half an ulp, at most 2^-8 of its
 magnitude) on top of the bf16 rounding of P in its products; heavily shared
 prefix tokens reach |dV| of several units, where the output rounding alone

@@ -196,10 +196,12 @@ def test_bwd_rows_match_dense():
 # ------------------------------------------------ gradient term magnitudes
 
 def _magnitudes_brute_force(tree, q, k, v, do, s):
-    """The absolute term sums of every gradient entry, by loops over each
-    query's parent chain (no dense mask, no matrix products): dQ_i sums
-    s P_ij dP_ij K_j and -s P_ij D_i K_j over visible j; dK_j and dV_j sum the
-    matching terms over the queries that see j."""
+    """The absolute sums of the elementary products behind every gradient
+    entry, by loops over each query's parent chain (no dense mask, no matrix
+    products): dQ_ic sums s P_ij dO_ie V_je K_jc over visible j and every e
+    (the dP terms), and s P_ij dO_ie P_ij' V_j'e K_jc over visible j, j' and
+    every e (the D terms); dK and dV sum the matching products over the
+    queries that see a key."""
     Np, hq, d = q.shape
     G = hq // k.shape[1]
     mq, mk, mv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
@@ -210,14 +212,14 @@ def _magnitudes_brute_force(tree, q, k, v, do, s):
             sc = np.array([s * float(np.dot(q[i, h], k[j, g])) for j in anc])
             p = np.exp(sc - sc.max())
             p /= p.sum()
-            o = sum(p[n] * v[j, g] for n, j in enumerate(anc))
-            D = float(np.dot(do[i, h], o))
+            dp_abs = [sum(abs(do[i, h, e] * v[j, g, e]) for e in range(d)) for j in anc]
+            d_abs = sum(abs(do[i, h, e] * p[n2] * v[j2, g, e])
+                        for e in range(d) for n2, j2 in enumerate(anc))
             for n, j in enumerate(anc):
-                dp = float(np.dot(do[i, h], v[j, g]))
                 for c in range(d):
-                    mq[i, h, c] += abs(s * p[n] * dp * k[j, g, c]) + abs(s * p[n] * D * k[j, g, c])
-                    mk[j, g, c] += abs(s * p[n] * dp * q[i, h, c]) + abs(s * p[n] * D * q[i, h, c])
-                    mv[j, g, c] += abs(p[n] * do[i, h, c])
+                    mq[i, h, c] += s * p[n] * (dp_abs[n] + d_abs) * abs(k[j, g, c])
+                    mk[j, g, c] += s * p[n] * (dp_abs[n] + d_abs) * abs(q[i, h, c])
+                    mv[j, g, c] += p[n] * abs(do[i, h, c])
     return mq, mk, mv
 
 
@@ -250,7 +252,7 @@ def test_bwd_magnitudes_bound_the_gradients():
 
 def test_bwd_magnitudes_single_token():
     """A token that sees only itself (P = 1, O = V, so dP = D): dQ = dK = 0
-    exactly, while the magnitudes are 2 s |dO.V| |K| and 2 s |dO.V| |Q|
+    exactly, while the magnitudes are 2 s (|dO|.|V|) |K| and 2 s (|dO|.|V|) |Q|
     (summed over the query heads of the group for K) and |dO| for V."""
     tree = oracle.build_forest([np.array([7], np.int32)], 128).trees[0]
     q, k, v, do = _tree_inputs(tree, 2, 1, 4, 15)
@@ -258,11 +260,11 @@ def test_bwd_magnitudes_single_token():
     dq, dk, _ = oracle.attn_bwd(tree, q, k, v, do)
     mq, mk, mv = oracle.attn_bwd_magnitudes(tree, q, k, v, do)
     for i in (0, 5, tree.n_padded - 1):         # the real token and two pad rows
-        dp = [abs(float(np.dot(do[i, h], v[i, 0]))) for h in range(2)]
+        a = [float(np.dot(np.abs(do[i, h]), np.abs(v[i, 0]))) for h in range(2)]
         np.testing.assert_allclose(dq[i], 0, atol=1e-12)
         np.testing.assert_allclose(dk[i], 0, atol=1e-12)
         for h in range(2):
-            np.testing.assert_allclose(mq[i, h], 2 * s * dp[h] * np.abs(k[i, 0]), rtol=1e-12)
-        np.testing.assert_allclose(mk[i, 0], 2 * s * (dp[0] * np.abs(q[i, 0]) + dp[1] * np.abs(q[i, 1])),
+            np.testing.assert_allclose(mq[i, h], 2 * s * a[h] * np.abs(k[i, 0]), rtol=1e-12)
+        np.testing.assert_allclose(mk[i, 0], 2 * s * (a[0] * np.abs(q[i, 0]) + a[1] * np.abs(q[i, 1])),
                                    rtol=1e-12)
         np.testing.assert_allclose(mv[i, 0], np.abs(do[i, 0]) + np.abs(do[i, 1]), rtol=1e-12)
