@@ -7,9 +7,12 @@ One step = the whole path over one batch of synthetic sequences:
   logprob/entropy gather when the workload has logits -- all through the C ABI.
 Q/K/V/dO/logits are resident in HBM before the timed region starts.
 
-Default workload: GRPO group packing (4 prompts x 512 tokens, 8 responses of
-U{128..1024} tokens, 8192-token trees, bf16, 32 query / 8 key-value heads,
-head_dim 128, forward + gather over a 32000-token vocab).
+Default workload: bimodal responses (64 prompts of 256 tokens x 4 samples,
+response lengths 70 % U{50..200} and 30 % U{800..2048}, 8192-token trees,
+bf16, 40 query / 8 key-value heads, head_dim 128): the 8K-token-tree
+configuration whose step has all three passes, attention forward, attention
+backward and the logprob/entropy gather over a 152064-token vocab.
+`--workload grpo` runs the GRPO group packing (forward + gather).
 
 Prints ONE JSON line.  `value` is the tree-attention effective TFLOP/s
 (forward, plus backward when timed): algorithmic FLOPs -- 4*d*Hq per visible
@@ -96,7 +99,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="grpo",
+    ap.add_argument("--workload", default="bimodal",
                     help="tiny | grpo | agentic | bimodal | long | long_control")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--rope", action="store_true",
