@@ -38,6 +38,7 @@
 #include "mfma.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace pst {
 namespace {
@@ -54,32 +55,11 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint8_t* base, int byte_off) 
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(base + byte_off));
 }
 
-// --------------------------------------------------------------------- D
-// D[h][row] = dO[row][h] . O[row][h]: 16 lanes per (row, head), 16 bytes each.
-__global__ __launch_bounds__(256) void bwd_dsum_bf16(const bf16_t* __restrict__ o,
-                                                     const bf16_t* __restrict__ dout,
-                                                     float* __restrict__ dsum, int Np, int hq) {
-  const int pair = blockIdx.x * 16 + (threadIdx.x >> 4);  // row * hq + h
-  const int part = threadIdx.x & 15;
-  float acc = 0.f;
-  if (pair < Np * hq) {
-    const size_t off = static_cast<size_t>(pair) * D + part * 8;
-    const uint4 ov = *reinterpret_cast<const uint4*>(o + off);
-    const uint4 dov = *reinterpret_cast<const uint4*>(dout + off);
-    const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w};
-    const uint32_t dw[4] = {dov.x, dov.y, dov.z, dov.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(dw[e] << 16), acc);
-      acc = fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(dw[e] & 0xffff0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (part == 0 && pair < Np * hq) {
-    const int row = pair / hq, h = pair - row * hq;
-    dsum[static_cast<size_t>(h) * Np + row] = acc;
-  }
+// Sum over the four lanes l % 16 + 16 g (g = 0..3), which hold one row's
+// four 32-wide slices of the head dimension in the 16x16 operand layouts.
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return sum_halves(__uint_as_float(a[0]) + __uint_as_float(a[1]));
 }
 
 // --------------------------------------------------------------------- dK, dV
@@ -117,16 +97,34 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x4_t& lo, const f32x4_t& hi) 
   return __builtin_convertvector(x, bf16x8_t);
 }
 
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
+// Eight waves: four pairs, pair p owning keys kbase .. kbase + 31 (kbase =
+// 128 kb + 32 p).  Wave p (role A) computes S = Q.K^T, masks it, forms
+// P = exp(S c - LSE) and accumulates dV^T += dO^T.P; it hands P (bf16, in
+// its accumulator layout) to wave p + 4 (role B) through LDS.  B computes
+// dP = dO.V^T (accumulators starting at -D) and, one 32-query sub-block
+// behind A, dS = P (dP - D) and dK^T += Q^T.dS.  Each wave holds one
+// accumulator set and one of K, V, so two waves share a SIMD and one's
+// exponentials run beside the other's MFMAs.  Every wave passes the same
+// barriers: two per 64-query step (at each 32-query sub-block; the first
+// also waits for the step's tiles), one after the loop for B's last
+// sub-block.  Four tile stages: B reads the previous sub-block's Q while
+// the step after next streams in.
+constexpr int kKvStages = 4;
+constexpr int kPexB = 2 * 1024;  // one pair's P of one sub-block: 2 chunks x 64 lanes x 16 B
+
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, TreeDev tr, int hq, int hkv, float c,
     float scale) {
-  // one named array per stage (Q tile, dO tile, LSE, D), so the compiler
-  // tells the in-flight DMA target from the stage being read
+  // one named array per stage, so the compiler tells the in-flight DMA
+  // target from the stage being read
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageB];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageB];
   __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStageB];
+  // P handed from A to B: [pair][sub-block parity][chunk kh][lane] x 16 B
+  __shared__ __attribute__((aligned(1024))) uint8_t pex[4 * 2 * kPexB];
 
   const int G = hq / hkv;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -136,30 +134,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const int li = lane % 16;  // key column of the 16x16 blocks
-  const int lg = lane / 16;  // 16-lane group: queries 4 lg .. 4 lg + 3 of each block
-  const int kbase = kb * kTile + 32 * wave;  // first key of this wave
-  int span_k[2];             // se - key of this lane's key in each half
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh) span_k[kh] = tr.se[kbase + 16 * kh + li] - (kbase + 16 * kh + li);
+  const int pair = wave & 3;
+  const bool roleA = wave < 4;  // wave-uniform
+  const int li = lane % 16;     // key column of the 16x16 blocks
+  const int lg = lane / 16;     // 16-lane group: queries 4 lg .. 4 lg + 3 of each block
+  const int kbase = kb * kTile + 32 * pair;  // first key of this pair
+  int span_k[2];  // se - key of this lane's key in each half (A); loaded below
   cint32* blk32 = cst(tr.blk32);
   const int smin = blk32[2 * (kbase >> 5)], smax = blk32[2 * (kbase >> 5) + 1];
-
-  // B operands K^T / V^T: key kbase + 16 kh + li, d = 32 s + 8 lg .. +7
-  bf16x8_t kf[2][4], vf[2][4];
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    const size_t off = (static_cast<size_t>(kbase + 16 * kh + li) * hkv + g) * D + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      kf[kh][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(k + off + 32 * s));
-      vf[kh][s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(v + off + 32 * s));
-    }
-  }
+  // B operands: K^T (A) or V^T (B), key kbase + 16 kh + li, d = 32 s + 8 lg
+  // .. +7; loaded below, once the first tiles are on their way
+  bf16x8_t kvf[2][4];
   // A operands Q / dO: query row li of a 16-row block, chunk 4 s + lg
   int roff[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) roff[s] = li * kRowB + (((4 * s + lg) ^ rsw(li)) << 4);
+  for (int s4 = 0; s4 < 4; ++s4) roff[s4] = li * kRowB + (((4 * s4 + lg) ^ rsw(li)) << 4);
   // transposed reads: lane i of group lg addresses token 4 lg + i / 4 at d = 4 (i % 4) .. +3
   int trv;
   {
@@ -168,22 +157,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
     trv = t * kRowB + ((((a >> 1) ^ rsw(t))) << 4) + ((a & 1) << 3);
   }
 
-  f32x4_t dkacc[8][2], dvacc[8][2];  // (d block db, key half kh)
+  f32x4_t acc[8][2];  // (d block db, key half kh): dV^T (A) or dK^T (B)
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      dkacc[db][kh] = f32x4_t{};
-      dvacc[db][kh] = f32x4_t{};
-    }
+  for (int db = 0; db < 8; ++db) acc[db][0] = acc[db][1] = f32x4_t{};
+  f32x4_t dpacc[2][2];  // B: dP - D of the sub-block it finishes next (query half q16, key half kh)
 
   const uint32_t q_bytes = static_cast<uint32_t>(hq) * D * 2;  // one token's Q (or dO) rows
   const int qhi = cst(tr.kb_qhi)[kb];
   const int n_steps = (qhi - kb + 1) * G * 2;
   // step -> (query block, head of the group, half): steps walk halves, then
-  // heads, then blocks.  Cursors for the step being computed and the one
-  // being prefetched advance by one step at a time (divisions by the group
-  // size only here, outside the loop).
+  // heads, then blocks; cursors advance one step at a time
   struct Cursor {
     int qb, r, half;
   };
@@ -205,8 +188,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
   // Every wave issues kDmaOps tile DMA instructions per step; waves 0 and 1
   // also one for LSE / D, first, so a wait for vmcnt(kDmaOps) lands every
   // step but the newest.
-  constexpr int kDmaOps = 2 * (kKvStep / 16);
-  const TileOff<kKvStep> qoff = tile_offsets<kKvStep>(q_bytes, wave, lane);
+  constexpr int kNw = 8;
+  constexpr int kDmaOps = 2 * TileOff<kKvStep, kNw>::kOps;
+  const TileOff<kKvStep, kNw> qoff = tile_offsets<kKvStep, kNw>(q_bytes, wave, lane);
   auto issue_loads = [&](const Cursor& cu, uint8_t* stg) {
     int h, q0;
     decode(cu, h, q0);
@@ -217,166 +201,222 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(
     else if (wave == 1)
       dma4_s(dsum + r0, 4u * lane, base + kStDd);
     const size_t row0 = static_cast<size_t>(q0) * q_bytes + static_cast<size_t>(h) * D * 2;
-    dma_tile_s<kKvStep>(reinterpret_cast<const char*>(q) + row0, qoff, base, wave);
-    dma_tile_s<kKvStep>(reinterpret_cast<const char*>(dout) + row0, qoff, base + kStDo, wave);
+    dma_tile_s<kKvStep, kNw>(reinterpret_cast<const char*>(q) + row0, qoff, base, wave);
+    dma_tile_s<kKvStep, kNw>(reinterpret_cast<const char*>(dout) + row0, qoff, base + kStDo, wave);
   };
+  auto empty_at = [&](int qlo) { return kbase > qlo + 31 || smax < qlo; };
+  uint8_t* const pex_pair = pex + pair * (2 * kPexB);
 
-  Cursor cur = cursor_at(0), pf = cursor_at(n_steps > 2 ? 2 : n_steps - 1);
-  auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
-    const uint8_t* ql = stg;
-    const uint8_t* dol = stg + kStDo;
+  // A: sub-block (stage stg, 32-query half qs at query qlo): S, mask, P,
+  // dV; P goes to pex slot `slot`
+  auto run_a = [&](const uint8_t* stg, int qs, int qlo, int slot) {
+    const bool full = kbase + 31 <= qlo && smin >= qlo + 31;
+    const uint8_t* qsl = stg + 32 * qs * kRowB;
+    const uint8_t* dosl = stg + kStDo + 32 * qs * kRowB;
     const float* lsl = reinterpret_cast<const float*>(stg + kStLs);
-    const float* ddl = reinterpret_cast<const float*>(stg + kStDd);
-    int h, q0;
-    decode(cur, h, q0);
-    advance(cur);
-    // step st staged by every wave, step st-1's LDS reads returned; a plain
-    // s_barrier, since a workgroup fence would also drain the newer prefetch
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaOps) : "memory");
-    // prefetch step min(st + 2, n_steps - 1)
-    issue_loads(pf, fill);
-    if (st + 3 < n_steps) advance(pf);
-
+    f32x4_t sacc[2][2];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const int qlo = q0 + 32 * qs;
-      const bool empty = kbase > qlo + 31 || smax < qlo;
-      if (empty) continue;
-      const bool full = kbase + 31 <= qlo && smin >= qlo + 31;
-      const uint8_t* qsl = ql + 32 * qs * kRowB;
-      const uint8_t* dosl = dol + 32 * qs * kRowB;
-
-      // S and dP blocks (query half q16, key half kh): eight chains.  The
-      // dP accumulators start at -D (register i of block (q16, kh) is query
-      // qlo + 16 q16 + 4 lg + i), so the MFMAs leave dP - D and dS = P (dP - D)
-      // costs one multiply per element.
-      f32x4_t sacc[2][2], dpacc[2][2];
+    for (int a = 0; a < 2; ++a) sacc[a][0] = sacc[a][1] = f32x4_t{};
+    auto qoffs = [&](int f) { return ((f & 1) ? kHalf16 : 0) + roff[f >> 1]; };
+    bf16x8_t qbuf[3];
+    qbuf[0] = lds_frag(qsl, qoffs(0));
+    qbuf[1] = lds_frag(qsl, qoffs(1));
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const float4 d4 = *reinterpret_cast<const float4*>(ddl + 32 * qs + 16 * a + 4 * lg);
-        const f32x4_t negd = {-d4.x, -d4.y, -d4.z, -d4.w};
+    for (int f = 0; f < 8; ++f) {
+      if (f + 2 < 8) qbuf[(f + 2) % 3] = lds_frag(qsl, qoffs(f + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      const int s4 = f >> 1, q16 = f & 1;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          sacc[a][b] = f32x4_t{};
-          dpacc[a][b] = negd;
-        }
-      }
-      // operand reads run two (s, q16) pairs ahead of their MFMAs (one wave
-      // per SIMD: nothing else hides the LDS latency); the scheduling
-      // barrier keeps the compiler from sinking the reads back to their use
-      auto qoffs = [&](int f) { return ((f & 1) ? kHalf16 : 0) + roff[f >> 1]; };
-      bf16x8_t qbuf[3], dbuf[3];
+      for (int kh = 0; kh < 2; ++kh) sacc[q16][kh] = mma16(qbuf[f % 3], kvf[kh][s4], sacc[q16][kh]);
+    }
+    // register i of block (q16, kh) is query qlo + 16 q16 + 4 lg + i, key
+    // kbase + 16 kh + li; key j sees query q iff (unsigned)(q - j) <= se[j] - j
+    if (!full) {
+      const int A = qlo + 4 * lg - kbase - li;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        qbuf[f] = lds_frag(qsl, qoffs(f));
-        dbuf[f] = lds_frag(dosl, qoffs(f));
-      }
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        if (f + 2 < 8) {
-          qbuf[(f + 2) % 3] = lds_frag(qsl, qoffs(f + 2));
-          dbuf[(f + 2) % 3] = lds_frag(dosl, qoffs(f + 2));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const int s = f >> 1, q16 = f & 1;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          sacc[q16][kh] = mma16(qbuf[f % 3], kf[kh][s], sacc[q16][kh]);
-          dpacc[q16][kh] = mma16(dbuf[f % 3], vf[kh][s], dpacc[q16][kh]);
-        }
-      }
-      // register i of block (q16, kh) is query qlo + 16 q16 + 4 lg + i, key
-      // kbase + 16 kh + li.  A partial block first sets its invisible scores
-      // to -inf (one branch per block, not a select per element of every
-      // block): key j sees query q iff (unsigned)(q - j) <= se[j] - j.
-      if (!full) {
-        const int A = qlo + 4 * lg - kbase - li;
-#pragma unroll
-        for (int q16 = 0; q16 < 2; ++q16)
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t dlt = static_cast<uint32_t>(A + 16 * q16 + i - 16 * kh);
-              sacc[q16][kh][i] = dlt <= static_cast<uint32_t>(span_k[kh]) ? sacc[q16][kh][i] : -INFINITY;
-            }
-      }
-      // P = exp(S c - LSE), 0 where masked; dS = P (dP - D)
-#pragma unroll
-      for (int q16 = 0; q16 < 2; ++q16) {
-        const float4 l4 = *reinterpret_cast<const float4*>(lsl + 32 * qs + 16 * q16 + 4 * lg);
-        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+      for (int q16 = 0; q16 < 2; ++q16)
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp2(fmaf(sacc[q16][kh][i], c, -lv[i]));
-            sacc[q16][kh][i] = e;
-            dpacc[q16][kh][i] = e * dpacc[q16][kh][i];
+            const uint32_t dlt = static_cast<uint32_t>(A + 16 * q16 + i - 16 * kh);
+            sacc[q16][kh][i] = dlt <= static_cast<uint32_t>(span_k[kh]) ? sacc[q16][kh][i] : -INFINITY;
           }
-      }
-      bf16x8_t pf[2], sf[2];
+    }
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        pf[kh] = pack8(sacc[0][kh], sacc[1][kh]);
-        sf[kh] = pack8(dpacc[0][kh], dpacc[1][kh]);
-      }
-      // dV^T += dO^T.P, dK^T += Q^T.dS
-      // transposed reads two d blocks ahead, held in place the same way
-      bf16x8_t obuf[3], tbuf[3];
+    for (int q16 = 0; q16 < 2; ++q16) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lsl + 32 * qs + 16 * q16 + 4 * lg);
+      const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        obuf[db] = lds_t16_frag(dosl, trv, db);
-        tbuf[db] = lds_t16_frag(qsl, trv, db);
-      }
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        if (db + 2 < 8) {
-          obuf[(db + 2) % 3] = lds_t16_frag(dosl, trv, db + 2);
-          tbuf[(db + 2) % 3] = lds_t16_frag(qsl, trv, db + 2);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i) sacc[q16][kh][i] = fast_exp2(fmaf(sacc[q16][kh][i], c, -lv[i]));
+    }
+    bf16x8_t pf[2];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          dvacc[db][kh] = mma16(obuf[db % 3], pf[kh], dvacc[db][kh]);
-          dkacc[db][kh] = mma16(tbuf[db % 3], sf[kh], dkacc[db][kh]);
-        }
+    for (int kh = 0; kh < 2; ++kh) {
+      pf[kh] = pack8(sacc[0][kh], sacc[1][kh]);
+      *reinterpret_cast<bf16x8_t*>(pex_pair + slot * kPexB + kh * 1024 + lane * 16) = pf[kh];
+    }
+    // dV^T += dO^T.P; transposed reads two d blocks ahead
+    bf16x8_t obuf[3];
+    obuf[0] = lds_t16_frag(dosl, trv, 0);
+    obuf[1] = lds_t16_frag(dosl, trv, 1);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      if (db + 2 < 8) obuf[(db + 2) % 3] = lds_t16_frag(dosl, trv, db + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) acc[db][kh] = mma16(obuf[db % 3], pf[kh], acc[db][kh]);
+    }
+  };
+  // B, first half of its work on a sub-block: dP - D into dpacc
+  auto run_b_dp = [&](const uint8_t* stg, int qs) {
+    const uint8_t* dosl = stg + kStDo + 32 * qs * kRowB;
+    const float* ddl = reinterpret_cast<const float*>(stg + kStDd);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const float4 d4 = *reinterpret_cast<const float4*>(ddl + 32 * qs + 16 * a + 4 * lg);
+      const f32x4_t negd = {-d4.x, -d4.y, -d4.z, -d4.w};
+      dpacc[a][0] = dpacc[a][1] = negd;
+    }
+    auto qoffs = [&](int f) { return ((f & 1) ? kHalf16 : 0) + roff[f >> 1]; };
+    bf16x8_t dbuf[3];
+    dbuf[0] = lds_frag(dosl, qoffs(0));
+    dbuf[1] = lds_frag(dosl, qoffs(1));
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      if (f + 2 < 8) dbuf[(f + 2) % 3] = lds_frag(dosl, qoffs(f + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      const int s4 = f >> 1, q16 = f & 1;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) dpacc[q16][kh] = mma16(dbuf[f % 3], kvf[kh][s4], dpacc[q16][kh]);
+    }
+  };
+  // B, second half: dS = P (dP - D) with A's P from pex slot `slot`, dK^T += Q^T.dS
+  auto run_b_dk = [&](const uint8_t* stg, int qs, int slot) {
+    const uint8_t* qsl = stg + 32 * qs * kRowB;
+    bf16x8_t sf[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const uint4 pw = *reinterpret_cast<const uint4*>(pex_pair + slot * kPexB + kh * 1024 + lane * 16);
+      const uint32_t w[4] = {pw.x, pw.y, pw.z, pw.w};
+      f32x4_t lo, hi;  // dS of query halves 0 and 1 (P in slots 0..3, 4..7)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        lo[2 * i] = __uint_as_float(w[i] << 16) * dpacc[0][kh][2 * i];
+        lo[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * dpacc[0][kh][2 * i + 1];
+        hi[2 * i] = __uint_as_float(w[2 + i] << 16) * dpacc[1][kh][2 * i];
+        hi[2 * i + 1] = __uint_as_float(w[2 + i] & 0xffff0000u) * dpacc[1][kh][2 * i + 1];
       }
+      sf[kh] = pack8(lo, hi);
+    }
+    bf16x8_t tbuf[3];
+    tbuf[0] = lds_t16_frag(qsl, trv, 0);
+    tbuf[1] = lds_t16_frag(qsl, trv, 1);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      if (db + 2 < 8) tbuf[(db + 2) % 3] = lds_t16_frag(qsl, trv, db + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) acc[db][kh] = mma16(tbuf[db % 3], sf[kh], acc[db][kh]);
     }
   };
 
-  // the K, V and subtree-end loads above complete here (empty asm uses pin
-  // them before the loop): the compiler's own waits for them would otherwise
-  // sit inside the loop and, not counting the assembly DMA, drain the
-  // prefetch
+  // the first two steps' tiles start streaming, then the K/V rows and
+  // subtree ends load beside them and complete here (empty asm uses pin
+  // them before the loop: the compiler does not count the assembly DMA, so
+  // its own waits for these loads, left inside the loop, would drain the
+  // prefetch)
+  issue_loads(cursor_at(0), stage0);
+  issue_loads(cursor_at(1), stage1);  // n_steps >= 2
+  {
+    const bf16_t* src = roleA ? k : v;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      span_k[kh] = tr.se[kbase + 16 * kh + li] - (kbase + 16 * kh + li);
+      const size_t off = (static_cast<size_t>(kbase + 16 * kh + li) * hkv + g) * D + 8 * lg;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        kvf[kh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + off + 32 * s4));
+    }
+  }
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     asm volatile("" ::"v"(span_k[kh]));
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) asm volatile("" ::"v"(kf[kh][s4]), "v"(vf[kh][s4]));
+    for (int s4 = 0; s4 < 4; ++s4) asm volatile("" ::"v"(kvf[kh][s4]));
   }
-  if (n_steps > 0) {
-    issue_loads(cursor_at(0), stage0);
-    issue_loads(cursor_at(1), stage1);  // n_steps >= 2
-  }
-  for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses stage st % 3
-    step(st, stage0, stage2);
-    if (st + 1 < n_steps) step(st + 1, stage1, stage0);
-    if (st + 2 < n_steps) step(st + 2, stage2, stage1);
-  }
+
+  // The step loop, instantiated once per role so that neither role's
+  // registers flow through the other's branches; both pass the same
+  // barriers in the same order (s_barrier counts arrivals, wherever they
+  // come from).
+  auto loop = [&](auto role) {
+    constexpr bool kA = decltype(role)::value;
+    Cursor cur = cursor_at(0), pf = cursor_at(n_steps > 2 ? 2 : n_steps - 1);
+    // B's pending sub-block: its stage, half, and whether it has any pair
+    const uint8_t* pend_stg = stage0;
+    int pend_qs = 0;
+    bool pend_live = false;
+    auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
+      int h, q0;
+      decode(cur, h, q0);
+      advance(cur);
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        if (qs == 0) {
+          // step st staged by every wave, the previous sub-block's P and
+          // LDS reads done; then prefetch step min(st + 2, n_steps - 1) into
+          // the stage step st - 2 used (free: B finished with it a step ago)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaOps) : "memory");
+          issue_loads(pf, fill);
+          if (st + 3 < n_steps) advance(pf);
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        const int qlo = q0 + 32 * qs;
+        const bool live = !empty_at(qlo);
+        if constexpr (kA) {
+          if (live) run_a(stg, qs, qlo, qs);
+        } else {
+          // each sub-block's P sits in the pex slot of its own half
+          if (pend_live) run_b_dk(pend_stg, pend_qs, pend_qs);
+          if (live) run_b_dp(stg, qs);
+          pend_stg = stg;
+          pend_qs = qs;
+          pend_live = live;
+        }
+      }
+    };
+    for (int st = 0; st < n_steps; st += kKvStages) {  // four-stage ring: step st uses stage st % 4
+      step(st, stage0, stage2);
+      if (st + 1 < n_steps) step(st + 1, stage1, stage3);
+      if (st + 2 < n_steps) step(st + 2, stage2, stage0);
+      if (st + 3 < n_steps) step(st + 3, stage3, stage1);
+    }
+    // B's last sub-block
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (!kA) {
+      if (pend_live) run_b_dk(pend_stg, pend_qs, pend_qs);
+    }
+  };
+  if (roleA)
+    loop(std::true_type{});
+  else
+    loop(std::false_type{});
   // the last steps' prefetch must land before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  bf16_t* const out = roleA ? dv : dk;
+  const float osc = roleA ? 1.f : scale;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     const size_t off = (static_cast<size_t>(kbase + 16 * kh + li) * hkv + g) * D + 4 * lg;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      store4<bf16_t>(dk + off + 16 * db, dkacc[db][kh][0] * scale, dkacc[db][kh][1] * scale,
-                     dkacc[db][kh][2] * scale, dkacc[db][kh][3] * scale);
-      store4<bf16_t>(dv + off + 16 * db, dvacc[db][kh][0], dvacc[db][kh][1], dvacc[db][kh][2],
-                     dvacc[db][kh][3]);
-    }
+    for (int db = 0; db < 8; ++db)
+      store4<bf16_t>(out + off + 16 * db, acc[db][kh][0] * osc, acc[db][kh][1] * osc,
+                     acc[db][kh][2] * osc, acc[db][kh][3] * osc);
   }
 }
 
@@ -400,8 +440,9 @@ constexpr int kQStageB = 2 * kQBuf + 4 * kQStep;
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
-    bf16_t* __restrict__ dq, TreeDev tr, int hq, int hkv, float c, float scale) {
+    const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ dsum, bf16_t* __restrict__ dq, TreeDev tr, int hq, int hkv, float c,
+    float scale) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kQStageB];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kQStageB];
   __shared__ __attribute__((aligned(1024))) uint8_t stage2[kQStageB];
@@ -443,21 +484,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     n_steps = cst(tr.step_ptr)[qb + 1] - cst(tr.step_ptr)[qb];
   }
 
-  // B operands Q^T / dO^T: query qlo + 16 qh + li, d = 32 s + 8 lg .. +7
+  // B operands Q^T / dO^T (query qlo + 16 qh + li, d = 32 s + 8 lg .. +7),
+  // the rows' LSE and D; loaded below, once the first tiles are on their way
   bf16x8_t qf[2][4], df[2][4];
   float lse2[2], dsq[2];
-#pragma unroll
-  for (int qh = 0; qh < 2; ++qh) {
-    const int row = qlo + 16 * qh + li;
-    const size_t off = (static_cast<size_t>(row) * hq + h) * D + 8 * lg;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      qf[qh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(q + off + 32 * s4));
-      df[qh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dout + off + 32 * s4));
-    }
-    lse2[qh] = lse[static_cast<size_t>(h) * tr.Np + row] * kLog2e;
-    dsq[qh] = dsum[static_cast<size_t>(h) * tr.Np + row];
-  }
   // A operands K / V: key row li (+16 for the second key half), chunk 4 s + lg
   int roff[4];
 #pragma unroll
@@ -595,17 +625,46 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     }
   };
 
-  // the register loads above complete here (empty asm uses pin them before
-  // the loop), so no compiler wait inside the loop drains the prefetch
+  // the first two steps' tiles start streaming, then the row operands load
+  // beside them and complete here (empty asm uses pin them before the
+  // loop), so no compiler wait inside the loop drains the prefetch
+  if (n_steps > 0) {
+    issue_loads(0, stage0);
+    issue_loads(n_steps > 1 ? 1 : 0, stage1);
+  }
+  // B operands Q^T / dO^T: query qlo + 16 qh + li, d = 32 s + 8 lg .. +7.
+  // D = rowsum(dO * O) of these rows is formed here (each (row, head) pair
+  // belongs to exactly one wave of one workgroup) and written for the dK/dV
+  // pass, which runs after this one.
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    const int row = qlo + 16 * qh + li;
+    const size_t off = (static_cast<size_t>(row) * hq + h) * D + 8 * lg;
+    float part = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      qf[qh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(q + off + 32 * s4));
+      df[qh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dout + off + 32 * s4));
+      const bf16x8_t of = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(o + off + 32 * s4));
+      const bf16x8_t& dd = df[qh][s4];
+      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 0, 1),
+                                             __builtin_shufflevector(dd, dd, 0, 1), part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 2, 3),
+                                             __builtin_shufflevector(dd, dd, 2, 3), part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 4, 5),
+                                             __builtin_shufflevector(dd, dd, 4, 5), part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 6, 7),
+                                             __builtin_shufflevector(dd, dd, 6, 7), part, false);
+    }
+    dsq[qh] = quad_sum(part);  // the four lanes of this row hold its 128 d
+    lse2[qh] = lse[static_cast<size_t>(h) * tr.Np + row] * kLog2e;
+    if (lg == 0) dsum[static_cast<size_t>(h) * tr.Np + row] = dsq[qh];
+  }
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
     asm volatile("" ::"v"(lse2[qh]), "v"(dsq[qh]));
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) asm volatile("" ::"v"(qf[qh][s4]), "v"(df[qh][s4]));
-  }
-  if (n_steps > 0) {
-    issue_loads(0, stage0);
-    issue_loads(n_steps > 1 ? 1 : 0, stage1);
   }
   for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses stage st % 3
     step(st, stage0, stage2);
@@ -638,28 +697,18 @@ hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v
                                      hipStream_t stream) {
   const float c = scale * kLog2e;
   float* dsum = static_cast<float*>(ws);
-  const unsigned pairs = static_cast<unsigned>(tr.Np) * hq;
-  hipLaunchKernelGGL(bwd_dsum_bf16, dim3((pairs + 15) / 16), dim3(256), 0, stream,
-                     static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), dsum, tr.Np, hq);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_bf16, dim3(static_cast<unsigned>(tr.nb) * hkv), dim3(256), 0, stream,
-                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum,
-                     static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), tr, hq, hkv, c, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // dQ in 32-query units of four heads for as many heads of each group as a
-  // multiple of four covers, 128-query blocks of one head for the rest, as
-  // the forward
+  // dQ first: it also forms D = rowsum(dO * O) for its rows into the
+  // workspace, which the dK/dV pass reads.  dQ runs in 32-query units of
+  // four heads for as many heads of each group as a multiple of four
+  // covers, 128-query blocks of one head for the rest, as the forward.
   const unsigned G = static_cast<unsigned>(hq / hkv), G4 = G / 4 * 4, GR = G - G4;
   const dim3 grid(static_cast<unsigned>(hkv) *
                   ((G4 / 4) * static_cast<unsigned>(tr.Np / 32) + GR * static_cast<unsigned>(tr.nb)));
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, static_cast<const bf16_t*>(q),
                        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-                       static_cast<const bf16_t*>(dout), lse, dsum, static_cast<bf16_t*>(dq), tr, hq,
-                       hkv, c, scale);
+                       static_cast<const bf16_t*>(o), static_cast<const bf16_t*>(dout), lse, dsum,
+                       static_cast<bf16_t*>(dq), tr, hq, hkv, c, scale);
   };
   if (GR == 0)
     launch(bwd_dq_bf16<1>);
@@ -667,6 +716,12 @@ hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v
     launch(bwd_dq_bf16<2>);
   else
     launch(bwd_dq_bf16<0>);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkdv_bf16, dim3(static_cast<unsigned>(tr.nb) * hkv), dim3(512), 0, stream,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                     static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum,
+                     static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), tr, hq, hkv, c, scale);
   return hipGetLastError();
 }
 

@@ -47,31 +47,33 @@ __device__ __forceinline__ void dma4_s(const void* base, uint32_t voff, uint32_t
 }
 
 // NROWS token rows of 256 bytes (row stride `stride` bytes in memory) ->
-// swizzled LDS tile; the four waves issue NROWS / 16 DMA instructions each,
-// instruction n covering rows 4n .. 4n+3.  tile_offsets gives the lane's
-// byte offsets within the rows (computed once), dma_tile_s issues the copies
-// from a tile's first row `base`.
-template <int NROWS>
+// swizzled LDS tile; the NW waves of a workgroup issue NROWS / (4 NW) DMA
+// instructions each, instruction n covering rows 4n .. 4n+3.  tile_offsets
+// gives the lane's byte offsets within the rows (computed once), dma_tile_s
+// issues the copies from a tile's first row `base`.
+template <int NROWS, int NW = 4>
 struct TileOff {
-  uint32_t v[NROWS / 16];
+  static_assert(NROWS % (4 * NW) == 0, "whole instructions per wave");
+  static constexpr int kOps = NROWS / (4 * NW);
+  uint32_t v[kOps];
 };
-template <int NROWS>
-__device__ __forceinline__ TileOff<NROWS> tile_offsets(uint32_t stride, int wave, int lane) {
-  TileOff<NROWS> o;
+template <int NROWS, int NW = 4>
+__device__ __forceinline__ TileOff<NROWS, NW> tile_offsets(uint32_t stride, int wave, int lane) {
+  TileOff<NROWS, NW> o;
 #pragma unroll
-  for (int i = 0; i < NROWS / 16; ++i) {
-    const int n = (NROWS / 16) * wave + i;
+  for (int i = 0; i < TileOff<NROWS, NW>::kOps; ++i) {
+    const int n = TileOff<NROWS, NW>::kOps * wave + i;
     const int r = 4 * n + (lane >> 4);
     o.v[i] = static_cast<uint32_t>(r) * stride + (static_cast<uint32_t>((lane & 15) ^ rsw(r)) << 4);
   }
   return o;
 }
-template <int NROWS>
-__device__ __forceinline__ void dma_tile_s(const char* base, const TileOff<NROWS>& o, uint32_t dst,
+template <int NROWS, int NW = 4>
+__device__ __forceinline__ void dma_tile_s(const char* base, const TileOff<NROWS, NW>& o, uint32_t dst,
                                            int wave) {
 #pragma unroll
-  for (int i = 0; i < NROWS / 16; ++i) {
-    const int n = (NROWS / 16) * wave + i;
+  for (int i = 0; i < TileOff<NROWS, NW>::kOps; ++i) {
+    const int n = TileOff<NROWS, NW>::kOps * wave + i;
     dma16_s(base, o.v[i], __builtin_amdgcn_readfirstlane(dst + n * 1024));
   }
 }
