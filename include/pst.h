@@ -220,6 +220,26 @@ int pst_tree_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype,
                       float softmax_scale, void* stream);
 
+/* pst_tree_attn_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight training loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the per-row sums that
+ * pst_tree_attn_bwd keeps in the caller's workspace held instead in a
+ * library-owned scratch array of 64 MiB per GPU (a static device array,
+ * present from the library's first use on a GPU until the process ends).
+ * The call allocates nothing; the caller still passes every input and
+ * output.  Shapes whose scratch (pst_tree_attn_bwd_workspace_bytes) exceeds
+ * 64 MiB -- hq * Np above 16 777 216 -- are refused with PST_ESHAPE before
+ * any HIP call.  All calls on one GPU share its scratch: two calls that
+ * overlap in time on one GPU (different streams, or host threads) race and
+ * give wrong results; serialize them.  The scratch needs no clearing (it is
+ * fully written before it is read).  Errors: as pst_tree_attn_bwd, and
+ * PST_EHIP if the scratch address cannot be obtained. */
+int pst_tree_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              const pst_tree_meta* meta, int32_t hq, int32_t hkv,
+                              int32_t head_dim, int32_t dtype, float softmax_scale,
+                              void* stream);
+
 /* ---- device: log-probabilities and entropies ------------------------------ */
 
 /* Per-sequence next-token log-probabilities and entropies from the packed

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     tree_attn_fwd,
     tree_attn_bwd,
     tree_attn_bwd_workspace_bytes,
+    tree_attn_bwd_noalloc,
     gather_tree_logprobs_entropy,
     gather_tree_logprobs_entropy_bwd,
     tree_rope,

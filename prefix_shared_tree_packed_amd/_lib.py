@@ -87,6 +87,10 @@ _SIGS = {
     "pst_tree_attn_bwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
                                     c_int32, c_int32, c_int32, c_int32, c_float, c_void_p]),
+    "pst_tree_attn_bwd_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_int32, c_int32, c_int32, c_int32, c_float,
+                                            c_void_p]),
     "pst_gather_tree_logprobs_entropy": (c_int32, [c_void_p, c_int64, c_int32, c_void_p,
                                                    c_void_p, c_void_p, c_void_p, c_void_p]),
     "pst_gather_tree_logprobs_entropy_bwd": (c_int32, [c_void_p, c_int64, c_int32, c_void_p,

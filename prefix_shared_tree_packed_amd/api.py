@@ -5,6 +5,7 @@ every computation happens in the library.  Names follow the C ABI:
     tree_meta_create(forest, tree, stream=None)    -> TreeMeta     (device upload)
     tree_attn_fwd(q, k, v, meta, ...)              -> (o, lse)
     tree_attn_bwd(q, k, v, o, lse, dout, meta, ...) -> (dq, dk, dv)
+    tree_attn_bwd_noalloc(q, k, v, o, lse, dout, meta, dq, dk, dv) -> (dq, dk, dv)
     gather_tree_logprobs_entropy(logits, meta, ...) -> (logprobs, entropy)
     gather_tree_logprobs_entropy_bwd(logits, meta, dlogprobs, dentropy) -> dlogits
     tree_rope(x, meta, theta=None, inverse=False)  -> x rotated in place
@@ -223,8 +224,9 @@ def tree_attn_bwd_workspace_bytes(meta: TreeMeta, hq: int, hkv: int, head_dim: i
     return n.value
 
 
-def tree_attn_bwd(q, k, v, o, lse, dout, meta: TreeMeta, softmax_scale: Optional[float] = None,
-                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+def _bwd_args(q, k, v, o, lse, dout, meta, dq, dk, dv):
+    """Checked arguments of the backward entry points: (hq, hkv, d, dtype
+    code, dq, dk, dv), outputs allocated when None."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout")):
         _dev_tensor(t, n)
@@ -241,15 +243,39 @@ def tree_attn_bwd(q, k, v, o, lse, dout, meta: TreeMeta, softmax_scale: Optional
     dq = torch.empty_like(q) if dq is None else _checked(dq, "dq", q.shape, q.dtype)
     dk = torch.empty_like(k) if dk is None else _checked(dk, "dk", k.shape, k.dtype)
     dv = torch.empty_like(v) if dv is None else _checked(dv, "dv", v.shape, v.dtype)
-    nbytes = tree_attn_bwd_workspace_bytes(meta, hq, hkv, d,
-                                           "bf16" if q.dtype == torch.bfloat16 else "f32")
+    return hq, hkv, d, code, dq, dk, dv
+
+
+def tree_attn_bwd(q, k, v, o, lse, dout, meta: TreeMeta, softmax_scale: Optional[float] = None,
+                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+    import torch
+    hq, hkv, d, code, dq, dk, dv = _bwd_args(q, k, v, o, lse, dout, meta, dq, dk, dv)
     if workspace is None:
+        nbytes = tree_attn_bwd_workspace_bytes(meta, hq, hkv, d,
+                                               "bf16" if q.dtype == torch.bfloat16 else "f32")
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     _dev_tensor(workspace, "workspace")
     check(_lib.load().pst_tree_attn_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), meta._h, hq, hkv, d, code,
+        float(softmax_scale or 0.0), c_void_p(_stream_ptr(stream))))
+    return dq, dk, dv
+
+
+def tree_attn_bwd_noalloc(q, k, v, o, lse, dout, meta: TreeMeta, dq, dk, dv,
+                          softmax_scale: Optional[float] = None, stream=None):
+    """tree_attn_bwd without a workspace: the library keeps the backward's
+    scratch in a 64 MiB array of its own per GPU and allocates nothing
+    (for code that cannot allocate, e.g. under graph capture).  The caller
+    passes dq, dk, dv.  Calls that overlap in time on one GPU race."""
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t is None:
+            raise ValueError(f"{n} must be given: tree_attn_bwd_noalloc allocates nothing")
+    hq, hkv, d, code, dq, dk, dv = _bwd_args(q, k, v, o, lse, dout, meta, dq, dk, dv)
+    check(_lib.load().pst_tree_attn_bwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), meta._h, hq, hkv, d, code,
         float(softmax_scale or 0.0), c_void_p(_stream_ptr(stream))))
     return dq, dk, dv
 

@@ -12,6 +12,7 @@
 #include <cstring>
 #include <numeric>
 #include <vector>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -22,6 +23,15 @@ using pst::check_tree;
 using pst::fail;
 using pst::fill_sizes;
 using pst::ok;
+
+// Device scratch of pst_tree_attn_bwd_noalloc: the backward's per-row sums
+// D = rowsum(dO * O) (float32 [hq, Np]), which pst_tree_attn_bwd takes in a
+// caller workspace.  One copy per GPU the library runs on, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (in
+// host code the name is a stand-in, not a device address): it uses the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;  // 64 MiB
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 // Device layout of one tree's metadata: a single int32 allocation holding
 // se [Np] | q_ptr [nb+1] | q_tile [n_tiles] | kb_qhi [nb] | fwd_order [nb] |
@@ -88,6 +98,29 @@ int check_ptrs(std::initializer_list<const void*> ps, const char* names) {
     if (!p) return fail(PST_EINVAL, std::string("NULL device pointer among ") + names);
     if (!aligned16(p)) return fail(PST_ESHAPE, std::string("device pointer not 16-byte aligned among ") + names);
   }
+  return PST_OK;
+}
+
+// Device address of `scratch` on the current device, looked up on the
+// device's first call and kept.
+int scratch_on_current_device(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PST_EINVAL, "device " + std::to_string(dev) + " beyond the scratch table");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(PST_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
   return PST_OK;
 }
 
@@ -377,6 +410,31 @@ int pst_tree_attn_bwd(const void* q, const void* k, const void* v, const void* o
       dtype, head_dim, q, k, v, o, lse, dout, dq, dk, dv, workspace,
       meta->dev, hq, hkv, resolve_scale(softmax_scale, head_dim), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tree_attn_bwd launch");
+  return ok();
+}
+
+int pst_tree_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              const pst_tree_meta* meta, int32_t hq, int32_t hkv,
+                              int32_t head_dim, int32_t dtype, float softmax_scale,
+                              void* stream) {
+  if (int e = check_attn_args(meta, hq, hkv, head_dim, dtype)) return e;
+  if (int e = check_ptrs({q, k, v, o, lse, dout, dq, dk, dv}, "q, k, v, o, lse, dout, dq, dk, dv"))
+    return e;
+  const size_t need = bwd_workspace_bytes(meta, hq, hkv, head_dim, dtype);
+  if (need > kNoAllocScratchBytes)
+    return fail(PST_ESHAPE, "these shapes need " + std::to_string(need) +
+                                " bytes of backward scratch, above the " +
+                                std::to_string(kNoAllocScratchBytes) +
+                                "-byte limit of pst_tree_attn_bwd_noalloc (use pst_tree_attn_bwd "
+                                "with a workspace)");
+  if (int e = check_meta_device(meta)) return e;
+  void* ws = nullptr;
+  if (int e = scratch_on_current_device(&ws)) return e;
+  const hipError_t e = pst::launch_attn_bwd(
+      dtype, head_dim, q, k, v, o, lse, dout, dq, dk, dv, ws, meta->dev, hq, hkv,
+      resolve_scale(softmax_scale, head_dim), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tree_attn_bwd_noalloc launch");
   return ok();
 }
 

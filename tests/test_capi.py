@@ -29,6 +29,8 @@ def test_device_entry_points_reject_null_meta():
     rc = lib.pst_tree_attn_bwd(p, p, p, p, p, p, p, p, p, p, 0, None, 32, 8, 128, 1, 0.0, None)
     assert _lib.ERRORS[rc] == "PST_EINVAL"
     assert b"NULL" in lib.pst_last_error()
+    rc = lib.pst_tree_attn_bwd_noalloc(p, p, p, p, p, p, p, p, p, None, 32, 8, 128, 1, 0.0, None)
+    assert _lib.ERRORS[rc] == "PST_EINVAL"
     rc = lib.pst_gather_tree_logprobs_entropy_bwd(p, 100, 1, None, p, p, None, p, None)
     assert _lib.ERRORS[rc] == "PST_EINVAL"
     rc = lib.pst_tree_rope(p, None, 8, 128, 1, 0.0, 0, None)
