@@ -2,10 +2,13 @@
 """Benchmark of the prefix-shared tree-training hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic sequences:
-  pack the sequences into tries (host, C++), upload each tree's metadata,
+  pack the sequences into tries (host, C++), upload the forest's metadata,
   tree attention forward (and backward when the workload trains), and the
   logprob/entropy gather when the workload has logits -- all through the C ABI.
-Q/K/V/dO/logits are resident in HBM before the timed region starts.
+Q/K/V/dO/logits are resident in HBM before the timed region starts.  The
+packing of upcoming batches runs on two worker threads ahead of the step
+that uploads them (as a data loader would), and the step re-uploads one
+metadata object in place, so the host keeps ahead of the GPU.
 
 Default workload: bimodal responses (64 prompts of 256 tokens x 4 samples,
 response lengths 70 % U{50..200} and 30 % U{800..2048}, 8192-token trees,
@@ -188,17 +191,36 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
+    # Host side of a step: the batch's forest is packed on worker threads
+    # (the C++ builder runs with the interpreter lock released), up to
+    # `ahead` batches before the step that uploads it, as a training data
+    # loader would; the step itself re-uploads the one metadata object in
+    # place (pst_forest_meta_update: no allocation, stream-ordered behind
+    # the previous step's kernels) and queues the kernels.  Every step
+    # still packs and uploads its own batch inside the timed region.
+    from concurrent.futures import ThreadPoolExecutor
+
+    def build():
+        return pst.build_tree(w.seqs, w.max_tokens_per_mb)
+
+    pool = ThreadPoolExecutor(max_workers=2)
+    ahead = 3
+    queued = [pool.submit(build) for _ in range(ahead)]
+    meta = pst.forest_meta_create(shape_forest, stream)
+
     def step(record):
-        forest = pst.build_tree(w.seqs, w.max_tokens_per_mb)
-        m = pst.forest_meta_create(forest, stream)
+        forest = queued.pop(0).result()
+        queued.append(pool.submit(build))
+        meta.update(forest, stream)
+        forest.close()
+        m = meta
         e = [torch.cuda.Event(enable_timing=True) for _ in range(8)] if record else None
         if record:
-            # The step is host-bound (tree build and metadata upload), so the
-            # GPU would reach e[0] idle and wait there for the forward's
-            # submission, timing the host's launch latency as kernel time.  A
-            # short spin (~0.1 ms, inside time the GPU would idle anyway)
-            # lets the host queue the forward first.  The later kernels of
-            # the step are queued while the forward runs.
+            # When the host only just keeps ahead (short steps, e.g. grpo's
+            # 0.6 ms), the GPU can reach e[0] idle and wait there for the
+            # forward's submission, timing the launch latency as kernel
+            # time.  A short spin (~0.1 ms of GPU time, counted in
+            # ms_per_step) lets the host queue the forward first.
             torch.cuda._sleep(200000)
             e[0].record(stream)
         pst.tree_attn_fwd(b["q"], b["k"], b["v"], m, out=b["o"], lse=b["lse"], stream=stream)
@@ -230,18 +252,12 @@ def main():
                                                  stream=stream)
             if record:
                 e[5].record(stream)
-        return forest, [m], [e] if record else []
-
-    def release(items):
-        torch.cuda.synchronize()
-        for forest, metas, _ in items:
-            for m in metas:
-                m.destroy()
-            forest.close()
+        return e
 
     log(f"{n_trees} trees; warmup {args.warmup} steps")
     for _ in range(args.warmup):
-        release([step(False)])
+        step(False)
+    torch.cuda.synchronize()
 
     # host packing alone, for the record
     t0 = time.perf_counter()
@@ -252,22 +268,24 @@ def main():
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    done = [step(True) for _ in range(args.steps)]
+    events = [step(True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) / args.steps * 1e3
+    for f in queued:
+        f.result().close()
+    pool.shutdown()
 
     fwd_ms, bwd_ms, gat_ms, gbw_ms, rope_ms = [], [], [], [], []
-    for _, _, evs in done:
-        for e in evs:
-            fwd_ms.append(e[0].elapsed_time(e[1]))
-            bwd_ms.append(e[1].elapsed_time(e[2]))
-            gat_ms.append(e[2].elapsed_time(e[3]))
-            if w.gather and args.gather_bwd:
-                gbw_ms.append(e[4].elapsed_time(e[5]))
-            if args.rope:
-                rope_ms.append(e[6].elapsed_time(e[7]))
-    release(done)
+    for e in events:
+        fwd_ms.append(e[0].elapsed_time(e[1]))
+        bwd_ms.append(e[1].elapsed_time(e[2]))
+        gat_ms.append(e[2].elapsed_time(e[3]))
+        if w.gather and args.gather_bwd:
+            gbw_ms.append(e[4].elapsed_time(e[5]))
+        if args.rope:
+            rope_ms.append(e[6].elapsed_time(e[7]))
+    meta.destroy()
 
     if args.mask:
         mask_t, mask_bytes = time_dense_mask(pst, torch, shape_forest, sizes, stream, args.steps)

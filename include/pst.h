@@ -178,6 +178,21 @@ int pst_tree_meta_create(const pst_forest* forest, int32_t tree, void* stream,
  * pst_tree_meta_create; sizes (pst_tree_meta_sizes) are sums over trees. */
 int pst_forest_meta_create(const pst_forest* forest, void* stream, pst_tree_meta** out);
 int pst_tree_meta_sizes(const pst_tree_meta* meta, pst_tree_sizes* out);
+/* Rebuild `meta` in place for `forest` (every tree, back to back, as
+ * pst_forest_meta_create), for a training loop that packs a new batch every
+ * step: the device allocation and the pinned staging memory are reused when
+ * large enough and grown otherwise, so in steady state the call allocates
+ * nothing and never synchronizes the device.  The upload is enqueued on
+ * `stream`: work already enqueued on that stream that reads the old
+ * metadata runs before the upload overwrites it (stream order); work on
+ * other streams that reads it must have completed.  Two pinned staging
+ * buffers alternate, so the host waits only for the upload issued two
+ * updates earlier.  Growing the device allocation synchronizes the device
+ * first.  If the call fails, `meta` is refused by every device entry point
+ * until an update succeeds.  Errors: PST_EINVAL (NULL, other device),
+ * PST_ENOMEM, PST_EHIP. */
+int pst_forest_meta_update(const pst_forest* forest, void* stream, pst_tree_meta* meta);
+
 /* Frees the metadata.  The caller first makes sure no work that reads it is
  * still queued (synchronize the stream it was used on). */
 int pst_tree_meta_destroy(pst_tree_meta* meta);

@@ -79,6 +79,7 @@ _SIGS = {
     "pst_tree_meta_create": (c_int32, [c_void_p, c_int32, c_void_p, POINTER(c_void_p)]),
     "pst_forest_meta_create": (c_int32, [c_void_p, c_void_p, POINTER(c_void_p)]),
     "pst_tree_meta_sizes": (c_int32, [c_void_p, POINTER(TreeSizes)]),
+    "pst_forest_meta_update": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "pst_tree_meta_destroy": (c_int32, [c_void_p]),
     "pst_tree_attn_fwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_int32, c_int32, c_int32, c_int32, c_float, c_void_p]),

@@ -3,6 +3,8 @@ every computation happens in the library.  Names follow the C ABI:
 
     build_tree(seqs, max_tokens_per_mb)            -> Forest       (host)
     tree_meta_create(forest, tree, stream=None)    -> TreeMeta     (device upload)
+    forest_meta_create(forest, stream=None)        -> TreeMeta     (all trees back to back)
+    TreeMeta.update(forest, stream=None)           -> re-upload into the same buffers
     tree_attn_fwd(q, k, v, meta, ...)              -> (o, lse)
     tree_attn_bwd(q, k, v, o, lse, dout, meta, ...) -> (dq, dk, dv)
     tree_attn_bwd_noalloc(q, k, v, o, lse, dout, meta, dq, dk, dv) -> (dq, dk, dv)
@@ -166,6 +168,21 @@ class TreeMeta:
         self.n_padded = self.sizes["n_padded"]
         self.n_tokens = self.sizes["n_tokens"]
         self.n_out = self.sizes["n_out"]
+
+    def update(self, forest: Forest, stream=None):
+        """Re-upload for another forest (all its trees) into the same device
+        and pinned buffers (pst_forest_meta_update): no allocation in steady
+        state.  Work queued on `stream` that reads the old metadata runs
+        first; work on other streams must have finished."""
+        s = _lib.TreeSizes()
+        lib = _lib.load()
+        check(lib.pst_forest_meta_update(forest._h, c_void_p(_stream_ptr(stream)), self._h))
+        check(lib.pst_tree_meta_sizes(self._h, byref(s)))
+        self.sizes = {f: getattr(s, f) for f, _ in s._fields_}
+        self.n_padded = self.sizes["n_padded"]
+        self.n_tokens = self.sizes["n_tokens"]
+        self.n_out = self.sizes["n_out"]
+        return self
 
     def destroy(self):
         """Frees the device copy; the caller has synchronized every stream

@@ -52,7 +52,7 @@ CXX_SOURCES = ["capi_host.cpp", "host/forest.cpp", "host/packing.cpp"]
 # the CPU-only sanitizer build of the host entry points (no HIP code in it)
 SAN_LIB = os.path.join(BUILD, "sanitize", "libpst_host_san.so")
 SAN_FLAGS = ["-O1", "-g", "-std=c++17", "-fPIC", "-Wall", "-fno-omit-frame-pointer",
-             "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-pthread",
              f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -42,14 +42,21 @@ static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 // tiles: (32-key block << 8) | the four 32-query sub-blocks' classes) |
 // unit_ptr [Np/32+1] | unit_steps [n_blk32] (the non-empty 32x32 blocks of
 // each 32-query unit: (32-key block << 2) | class) | unit_order [Np/32] |
-// pos [Np] (depth
-// of every row, 0 for pad rows), every section starting on a 16-byte
-// boundary.  The pinned staging copy is
-// kept until destroy so the asynchronous upload never reads freed memory.
+// pos [Np] (depth of every row, 0 for pad rows), every section starting on
+// a 16-byte boundary.  It is filled in one of two pinned staging buffers and
+// uploaded asynchronously; the uploads alternate between the two, and an
+// event after each upload says when its staging buffer may be refilled, so
+// an update waits only for the upload issued two updates before.
 struct pst_tree_meta {
   int device = -1;
-  int32_t* dbuf = nullptr;
-  int32_t* hbuf = nullptr;
+  int32_t* dbuf = nullptr;   // device words (capacity dcap)
+  size_t dcap = 0;
+  int32_t* hbuf[2] = {nullptr, nullptr};  // pinned staging (capacity hcap[i])
+  size_t hcap[2] = {0, 0};
+  hipEvent_t uploaded[2] = {nullptr, nullptr};  // after the upload from hbuf[i]
+  bool pending[2] = {false, false};             // uploaded[i] recorded
+  int next = 0;                                 // staging buffer of the next update
+  bool valid = false;  // false while an upload is in progress or after one failed
   size_t n_words = 0;
   pst_tree_sizes sizes{};
   pst::TreeDev dev{};
@@ -65,7 +72,11 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-int check_meta_device(const pst_tree_meta* meta) {
+// The metadata lives on the current device and, unless only its device is
+// asked about, holds a complete upload.
+int check_meta_device(const pst_tree_meta* meta, bool need_valid = true) {
+  if (need_valid && !meta->valid)
+    return fail(PST_EINVAL, "tree metadata is not usable: its last update failed");
   int dev = -1;
   const hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -128,11 +139,13 @@ float resolve_scale(float s, int32_t head_dim) {
   return s > 0.f ? s : 1.0f / std::sqrt(static_cast<float>(head_dim));
 }
 
-// Uploads the metadata of `trees`, laid back to back in the given order:
-// rows of tree t follow the padded rows of the trees before it, its outputs
-// follow theirs.  Attention never crosses trees, so the concatenation is
-// itself a valid packed layout and one launch serves all of them.
-int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tree_meta** out) {
+// Builds the metadata of `trees`, laid back to back in the given order, and
+// uploads it into `m` on `stream`, reusing m's buffers when they are large
+// enough: rows of tree t follow the padded rows of the trees before it, its
+// outputs follow theirs.  Attention never crosses trees, so the
+// concatenation is itself a valid packed layout and one launch serves all of
+// them.
+int upload_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tree_meta* m) {
   int64_t Np = 0, nb = 0, n_tiles = 0, n_out = 0, n_steps = 0, n_blk32 = 0;
   pst_tree_sizes sz{};
   // the four 32-query sub-blocks' classes of column ks of a tile
@@ -188,25 +201,51 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   const size_t o_pos = off;       off += round4(Np);
   const size_t words = off;
 
-  pst_tree_meta* m = new (std::nothrow) pst_tree_meta;
-  if (!m) return fail(PST_ENOMEM, "out of host memory");
-  hipError_t e = hipGetDevice(&m->device);
-  if (e != hipSuccess) {
-    delete m;
-    return hip_fail(e, "hipGetDevice");
+  // until this upload completes, device calls refuse the metadata (a failure
+  // below may have released the buffers its device view points into)
+  m->valid = false;
+  const int buf = m->next;
+  // the staging buffer's previous upload must have read it before refilling
+  if (m->pending[buf]) {
+    hipError_t e = hipEventSynchronize(m->uploaded[buf]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    m->pending[buf] = false;
   }
-  e = hipHostMalloc(reinterpret_cast<void**>(&m->hbuf), words * sizeof(int32_t), hipHostMallocDefault);
-  if (e != hipSuccess) {
-    delete m;
-    return fail(PST_ENOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  if (m->hcap[buf] < words) {
+    if (m->hbuf[buf]) {
+      hipError_t e = hipHostFree(m->hbuf[buf]);
+      m->hbuf[buf] = nullptr;
+      m->hcap[buf] = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipHostFree");
+    }
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&m->hbuf[buf]), words * sizeof(int32_t),
+                                 hipHostMallocDefault);
+    if (e != hipSuccess) {
+      m->hbuf[buf] = nullptr;
+      return fail(PST_ENOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+    }
+    m->hcap[buf] = words;
   }
-  e = hipMalloc(reinterpret_cast<void**>(&m->dbuf), words * sizeof(int32_t));
-  if (e != hipSuccess) {
-    (void)hipHostFree(m->hbuf);
-    delete m;
-    return fail(PST_ENOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+  if (m->dcap < words) {
+    if (m->dbuf) {
+      // queued work on any stream may still read the old words
+      hipError_t e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      e = hipFree(m->dbuf);
+      m->dbuf = nullptr;
+      m->dcap = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&m->dbuf), words * sizeof(int32_t));
+    if (e != hipSuccess) {
+      m->dbuf = nullptr;
+      return fail(PST_ENOMEM, std::string("hipMalloc: ") + hipGetErrorString(e));
+    }
+    m->dcap = words;
   }
-  int32_t* h = m->hbuf;
+  m->min_target = 0;
+  m->max_target = -1;
+  int32_t* h = m->hbuf[buf];
   std::memset(h, 0, words * sizeof(int32_t));
   int32_t row0 = 0, blk0 = 0, tile0 = 0, out0 = 0;
   bool any_target = false;
@@ -308,14 +347,14 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
     });
     std::copy(uord.begin(), uord.end(), h + o_uord);
   }
-  e = hipMemcpyAsync(m->dbuf, h, words * sizeof(int32_t), hipMemcpyHostToDevice,
-                     static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    (void)hipFree(m->dbuf);
-    (void)hipHostFree(m->hbuf);
-    delete m;
-    return hip_fail(e, "hipMemcpyAsync");
-  }
+  hipError_t e = hipMemcpyAsync(m->dbuf, h, words * sizeof(int32_t), hipMemcpyHostToDevice,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipEventRecord(m->uploaded[buf], static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  m->pending[buf] = true;
+  m->next = buf ^ 1;
+  m->valid = true;
   m->n_words = words;
   m->sizes = sz;
   int32_t* d = m->dbuf;
@@ -323,6 +362,42 @@ int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
                         d + o_bord, d + o_rptr, d + o_opos,  d + o_otgt, d + o_blk, d + o_qcls,
                         d + o_pos,  d + o_sptr, d + o_step, d + o_uptr, d + o_ustep,
                         d + o_uord, sz.n_tokens, sz.n_padded, sz.n_blocks, sz.n_tiles};
+  return PST_OK;
+}
+
+// Frees everything `m` holds (the caller has synchronized its uploads).
+int release_meta(pst_tree_meta* m) {
+  hipError_t first = hipSuccess;
+  auto keep = [&](hipError_t e) {
+    if (first == hipSuccess) first = e;
+  };
+  if (m->dbuf) keep(hipFree(m->dbuf));
+  for (int i = 0; i < 2; ++i) {
+    if (m->hbuf[i]) keep(hipHostFree(m->hbuf[i]));
+    if (m->uploaded[i]) keep(hipEventDestroy(m->uploaded[i]));
+  }
+  delete m;
+  if (first != hipSuccess) return hip_fail(first, "releasing tree metadata");
+  return PST_OK;
+}
+
+// A new metadata object on the current device holding the upload of `trees`.
+int create_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tree_meta** out) {
+  pst_tree_meta* m = new (std::nothrow) pst_tree_meta;
+  if (!m) return fail(PST_ENOMEM, "out of host memory");
+  hipError_t e = hipGetDevice(&m->device);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i)
+    e = hipEventCreateWithFlags(&m->uploaded[i], hipEventDisableTiming);
+  if (e != hipSuccess) {
+    const int r = hip_fail(e, "creating tree metadata");
+    (void)release_meta(m);
+    return r;
+  }
+  if (int r = upload_meta(trees, stream, m)) {
+    const std::string msg = pst_last_error();
+    (void)release_meta(m);
+    return fail(r, msg);
+  }
   *out = m;
   return ok();
 }
@@ -354,13 +429,18 @@ int pst_tree_meta_sizes(const pst_tree_meta* meta, pst_tree_sizes* out) {
   return ok();
 }
 
+int pst_forest_meta_update(const pst_forest* forest, void* stream, pst_tree_meta* meta) {
+  if (!forest || !meta) return fail(PST_EINVAL, "NULL argument");
+  if (int e = check_meta_device(meta, false)) return e;
+  std::vector<const pst::Tree*> trees;
+  for (const pst::Tree& t : forest->f.trees) trees.push_back(&t);
+  if (int e = upload_meta(trees, stream, meta)) return e;
+  return ok();
+}
+
 int pst_tree_meta_destroy(pst_tree_meta* meta) {
   if (!meta) return ok();
-  hipError_t e1 = hipFree(meta->dbuf);
-  hipError_t e2 = hipHostFree(meta->hbuf);
-  delete meta;
-  if (e1 != hipSuccess) return hip_fail(e1, "hipFree");
-  if (e2 != hipSuccess) return hip_fail(e2, "hipHostFree");
+  if (int e = release_meta(meta)) return e;
   return ok();
 }
 

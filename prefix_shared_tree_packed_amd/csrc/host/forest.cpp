@@ -3,7 +3,11 @@
 #include "forest.h"
 
 #include <algorithm>
+#include <atomic>
+#include <exception>
 #include <numeric>
+#include <system_error>
+#include <thread>
 #include <unordered_map>
 
 namespace pst {
@@ -62,7 +66,9 @@ struct Trie {
     return c;
   }
 
-  int64_t shared_prefix(const int32_t* s, int64_t len) const {
+  // Length of the longest prefix of s already in the trie; *end is the node
+  // of its last token (the root for an empty prefix).
+  int64_t shared_prefix(const int32_t* s, int64_t len, int32_t* end) const {
     int32_t cur = 0;
     int64_t n = 0;
     for (; n < len; ++n) {
@@ -70,17 +76,21 @@ struct Trie {
       if (c < 0) break;
       cur = c;
     }
+    *end = cur;
     return n;
   }
 
-  // Inserts the sequence and records the trie node of each of its tokens.
-  void insert(const int32_t* s, int64_t len, int32_t* path) {
-    int32_t cur = 0;
-    for (int64_t i = 0; i < len; ++i) {
-      int32_t c = child(cur, s[i]);
-      if (c < 0) c = add_child(cur, s[i]);
-      cur = c;
+  // Inserts the sequence, whose first `shared` tokens are already in the
+  // trie ending at node `at`, and records the trie node of each token.
+  void insert(const int32_t* s, int64_t len, int64_t shared, int32_t at, int32_t* path) {
+    for (int32_t i = static_cast<int32_t>(shared) - 1, c = at; i >= 0; --i) {
       path[i] = c;
+      c = nodes[c].parent;
+    }
+    int32_t cur = at;
+    for (int64_t i = shared; i < len; ++i) {
+      cur = add_child(cur, s[i]);
+      path[i] = cur;
     }
     nodes[cur].n_ending++;
   }
@@ -352,33 +362,65 @@ int build_forest(const int32_t* tokens, const int64_t* offsets, int32_t n_seqs,
 
   std::vector<int32_t> path(static_cast<size_t>(offsets[n_seqs]));
   std::vector<Trie> tries;
+  // a trie never holds more than min(capacity, all tokens) nodes
+  const size_t trie_cap = static_cast<size_t>(std::min<int64_t>(capacity, total)) + 1;
   for (int32_t s : order) {
     const int32_t* seq = tokens + offsets[s];
     const int64_t len = offsets[s + 1] - offsets[s];
-    int32_t chosen = -1;
+    int32_t chosen = -1, at = 0;
+    int64_t shared = 0;
     for (size_t t = 0; t < tries.size(); ++t) {
-      const int64_t cost = len - tries[t].shared_prefix(seq, len);
-      if (tries[t].count + cost <= capacity) {
-        tries[t].count += cost;
+      int32_t end = 0;
+      const int64_t sp = tries[t].shared_prefix(seq, len, &end);
+      if (tries[t].count + (len - sp) <= capacity) {
+        tries[t].count += len - sp;
         chosen = static_cast<int32_t>(t);
+        shared = sp;
+        at = end;
         break;
       }
     }
     if (chosen < 0) {
       tries.emplace_back();
+      tries.back().nodes.reserve(trie_cap);
       chosen = static_cast<int32_t>(tries.size() - 1);
       tries.back().count = len;
     }
-    tries[chosen].insert(seq, len, path.data() + offsets[s]);
+    tries[chosen].insert(seq, len, shared, at, path.data() + offsets[s]);
     tries[chosen].members.push_back(s);
     out.seq_tree[s] = chosen;
     out.causal_pairs += len * (len + 1) / 2;
   }
 
+  // Trees are independent from here on: flatten them on a few threads (the
+  // calling thread included), taking trees in order from a shared counter.
   out.trees.resize(tries.size());
-  for (size_t t = 0; t < tries.size(); ++t)
-    flatten(tries[t], static_cast<int32_t>(t), tokens, offsets, path,
-            pad_to_maximum ? capacity : 0, out.trees[t]);
+  const int32_t n_trees = static_cast<int32_t>(tries.size());
+  std::atomic<int32_t> next{0};
+  std::exception_ptr failed;
+  std::atomic<bool> any_failed{false};
+  auto work = [&]() {
+    for (int32_t t = next++; t < n_trees; t = next++) {
+      try {
+        flatten(tries[t], t, tokens, offsets, path, pad_to_maximum ? capacity : 0, out.trees[t]);
+      } catch (...) {
+        if (!any_failed.exchange(true)) failed = std::current_exception();
+      }
+    }
+  };
+  // at most 8 threads: callers may run several builds at once
+  const int32_t hw = static_cast<int32_t>(std::min(8u, std::max(1u, std::thread::hardware_concurrency())));
+  std::vector<std::thread> helpers;
+  for (int32_t i = 1; i < std::min(n_trees, hw); ++i) {
+    try {
+      helpers.emplace_back(work);
+    } catch (const std::system_error&) {
+      break;  // no more threads: the others (and this one) take the rest
+    }
+  }
+  work();
+  for (std::thread& th : helpers) th.join();
+  if (failed) std::rethrow_exception(failed);
   return kBuildOk;
 }
 

@@ -37,6 +37,8 @@ def test_device_entry_points_reject_null_meta():
     assert _lib.ERRORS[rc] == "PST_EINVAL"
     rc = lib.pst_tree_dense_mask(None, 0, p, None)
     assert _lib.ERRORS[rc] == "PST_EINVAL"
+    rc = lib.pst_forest_meta_update(None, None, None)
+    assert _lib.ERRORS[rc] == "PST_EINVAL"
 
 
 def test_build_rejects_unknown_flags():

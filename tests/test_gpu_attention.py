@@ -378,3 +378,47 @@ def test_output_buffers_checked(gpu_lib):
         torch.cuda.synchronize()
     finally:
         case.close()
+
+
+def test_forest_meta_update_matches_fresh(gpu_lib):
+    """One metadata object re-uploaded in place for three different forests
+    (growing, then shrinking), with each forest's forward, backward and
+    gather queued right after its update and no synchronization in between:
+    every result equals, bit for bit, the one computed with fresh metadata
+    of that forest (stream order keeps each upload behind the kernels that
+    read the previous one; the two pinned staging buffers alternate)."""
+    import torch
+    rng = np.random.default_rng(31)
+    seq_sets = [prompt_groups(rng, 2, 150, 3, 20, 200), prompt_groups(rng, 4, 300, 4, 50, 500),
+                prompt_groups(rng, 1, 60, 2, 10, 40)]
+    forests = [gpu_lib.build_tree(s, 1024) for s in seq_sets]
+    meta = gpu_lib.forest_meta_create(forests[0])
+    results, inputs = [], []
+    try:
+        for i, f in enumerate(forests):
+            if i:
+                meta.update(f)
+            Np = meta.n_padded
+            print(f"meta update case {i}: Np={Np}", flush=True)
+            q, k, v, do = attn_inputs(Np, 8, 2, 128, "bf16", 80 + i, with_dout=True)
+            logits = torch.randn(Np, 1024, device="cuda").to(torch.bfloat16)
+            o, lse = gpu_lib.tree_attn_fwd(q, k, v, meta)
+            grads = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, meta)
+            lp, ent = gpu_lib.gather_tree_logprobs_entropy(logits, meta)
+            results.append((o, lse, *grads, lp, ent))
+            inputs.append((q, k, v, do, logits))
+        torch.cuda.synchronize()
+        for f, (q, k, v, do, logits), got in zip(forests, inputs, results):
+            fresh = gpu_lib.forest_meta_create(f)
+            o, lse = gpu_lib.tree_attn_fwd(q, k, v, fresh)
+            grads = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, fresh)
+            lp, ent = gpu_lib.gather_tree_logprobs_entropy(logits, fresh)
+            torch.cuda.synchronize()
+            for a, b in zip(got, (o, lse, *grads, lp, ent)):
+                assert torch.equal(a, b)
+            fresh.destroy()
+    finally:
+        torch.cuda.synchronize()
+        meta.destroy()
+        for f in forests:
+            f.close()
