@@ -634,8 +634,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   }
   // B operands Q^T / dO^T: query qlo + 16 qh + li, d = 32 s + 8 lg .. +7.
   // D = rowsum(dO * O) of these rows is formed here (each (row, head) pair
-  // belongs to exactly one wave of one workgroup) and written for the dK/dV
-  // pass, which runs after this one.
+  // belongs to exactly one wave of one workgroup) and written with dQ at
+  // the end, for the dK/dV pass, which runs after this one (a store here
+  // would hold the in-order vmcnt waits of the loop's first steps).
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
     const int row = qlo + 16 * qh + li;
@@ -658,7 +659,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     }
     dsq[qh] = quad_sum(part);  // the four lanes of this row hold its 128 d
     lse2[qh] = lse[static_cast<size_t>(h) * tr.Np + row] * kLog2e;
-    if (lg == 0) dsum[static_cast<size_t>(h) * tr.Np + row] = dsq[qh];
   }
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
@@ -676,6 +676,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
 
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
+    if (lg == 0) dsum[static_cast<size_t>(h) * tr.Np + qlo + 16 * qh + li] = dsq[qh];
     bf16_t* op = dq + (static_cast<size_t>(qlo + 16 * qh + li) * hq + h) * D + 4 * lg;
 #pragma unroll
     for (int db = 0; db < 8; ++db)
