@@ -219,9 +219,9 @@ def main():
             # When the host only just keeps ahead (short steps, e.g. grpo's
             # 0.6 ms), the GPU can reach e[0] idle and wait there for the
             # forward's submission, timing the launch latency as kernel
-            # time.  A short spin (~0.1 ms of GPU time, counted in
+            # time.  A short spin (~0.05 ms of GPU time, counted in
             # ms_per_step) lets the host queue the forward first.
-            torch.cuda._sleep(200000)
+            torch.cuda._sleep(100000)
             e[0].record(stream)
         pst.tree_attn_fwd(b["q"], b["k"], b["v"], m, out=b["o"], lse=b["lse"], stream=stream)
         if record:

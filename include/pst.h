@@ -334,8 +334,9 @@ enum { PST_MASK_U8 = 0, PST_MASK_ADD_F32 = 1, PST_MASK_ADD_BF16 = 2 };
  * subtree_end[j] in preorder); pad rows see only themselves.
  *   format  PST_MASK_U8: uint8, 1 visible, 0 hidden;
  *           PST_MASK_ADD_F32 / PST_MASK_ADD_BF16: additive, 0 visible, -inf hidden.
- * Errors: PST_EINVAL, PST_EDTYPE (unknown format), PST_ESHAPE (Np above
- * 2 097 120 or misaligned out), PST_EHIP. */
+ * Any Np the metadata holds is covered (row groups are strided over a
+ * capped grid).  Errors: PST_EINVAL, PST_EDTYPE (unknown format),
+ * PST_ESHAPE (misaligned out), PST_EHIP. */
 int pst_tree_dense_mask(const pst_tree_meta* meta, int32_t format, void* out, void* stream);
 
 /* ---- host: micro-batch / rank allocation -------------------------------- */

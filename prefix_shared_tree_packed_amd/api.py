@@ -49,23 +49,26 @@ def _ptr_or_null(t):
     return 0 if t is None else t.data_ptr()
 
 
-def _dev_tensor(t, name):
-    import torch
+def _dev_tensor(t, name, dev=None):
+    """A contiguous tensor on the current device (`dev`: its index, when the
+    caller already has it; looked up once per call otherwise)."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if t.device.index != torch.cuda.current_device():
-        raise ValueError(f"{name} is on {t.device}, not the current device "
-                         f"cuda:{torch.cuda.current_device()}")
+    if dev is None:
+        import torch
+        dev = torch.cuda.current_device()
+    if t.get_device() != dev:
+        raise ValueError(f"{name} is on cuda:{t.get_device()}, not the current device cuda:{dev}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
 
 
-def _checked(t, name, shape, dtype):
+def _checked(t, name, shape, dtype, dev=None):
     """A caller-supplied buffer: a contiguous device tensor of exactly this
     shape and dtype (the library sees only its pointer, so a smaller or
     differently typed buffer would be read or written out of bounds)."""
-    _dev_tensor(t, name)
+    _dev_tensor(t, name, dev)
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype} {list(shape)}, got {t.dtype} {list(t.shape)}")
     return t
@@ -212,8 +215,9 @@ def forest_meta_create(forest: Forest, stream=None) -> TreeMeta:
 def tree_attn_fwd(q, k, v, meta: TreeMeta, softmax_scale: Optional[float] = None,
                   out=None, lse=None, stream=None):
     import torch
+    dev = torch.cuda.current_device()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev_tensor(t, n)
+        _dev_tensor(t, n, dev)
     Np, hq, d = q.shape
     hkv = k.shape[1]
     if k.shape != (Np, hkv, d) or v.shape != k.shape or Np != meta.n_padded:
@@ -222,9 +226,9 @@ def tree_attn_fwd(q, k, v, meta: TreeMeta, softmax_scale: Optional[float] = None
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     code = _dtype_code(q)
-    out = torch.empty_like(q) if out is None else _checked(out, "out", q.shape, q.dtype)
+    out = torch.empty_like(q) if out is None else _checked(out, "out", q.shape, q.dtype, dev)
     lse = (torch.empty((hq, Np), dtype=torch.float32, device=q.device) if lse is None
-           else _checked(lse, "lse", (hq, Np), torch.float32))
+           else _checked(lse, "lse", (hq, Np), torch.float32, dev))
     check(_lib.load().pst_tree_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         lse.data_ptr(), meta._h, hq, hkv, d, code,
@@ -245,8 +249,9 @@ def _bwd_args(q, k, v, o, lse, dout, meta, dq, dk, dv):
     """Checked arguments of the backward entry points: (hq, hkv, d, dtype
     code, dq, dk, dv), outputs allocated when None."""
     import torch
+    dev = torch.cuda.current_device()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout")):
-        _dev_tensor(t, n)
+        _dev_tensor(t, n, dev)
     Np, hq, d = q.shape
     hkv = k.shape[1]
     if (k.shape != (Np, hkv, d) or v.shape != k.shape or o.shape != q.shape
@@ -257,9 +262,9 @@ def _bwd_args(q, k, v, o, lse, dout, meta, dq, dk, dv):
     if lse.dtype != torch.float32:
         raise ValueError(f"lse must be float32, got {lse.dtype}")
     code = _dtype_code(q)
-    dq = torch.empty_like(q) if dq is None else _checked(dq, "dq", q.shape, q.dtype)
-    dk = torch.empty_like(k) if dk is None else _checked(dk, "dk", k.shape, k.dtype)
-    dv = torch.empty_like(v) if dv is None else _checked(dv, "dv", v.shape, v.dtype)
+    dq = torch.empty_like(q) if dq is None else _checked(dq, "dq", q.shape, q.dtype, dev)
+    dk = torch.empty_like(k) if dk is None else _checked(dk, "dk", k.shape, k.dtype, dev)
+    dv = torch.empty_like(v) if dv is None else _checked(dv, "dv", v.shape, v.dtype, dev)
     return hq, hkv, d, code, dq, dk, dv
 
 
@@ -271,7 +276,7 @@ def tree_attn_bwd(q, k, v, o, lse, dout, meta: TreeMeta, softmax_scale: Optional
         nbytes = tree_attn_bwd_workspace_bytes(meta, hq, hkv, d,
                                                "bf16" if q.dtype == torch.bfloat16 else "f32")
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _dev_tensor(workspace, "workspace")
+    _dev_tensor(workspace, "workspace", torch.cuda.current_device())
     check(_lib.load().pst_tree_attn_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
@@ -297,11 +302,11 @@ def tree_attn_bwd_noalloc(q, k, v, o, lse, dout, meta: TreeMeta, dq, dk, dv,
     return dq, dk, dv
 
 
-def _row_stats(t, meta, name="row_stats"):
+def _row_stats(t, meta, name="row_stats", dev=None):
     import torch
     if t is None:
         return None
-    return _checked(t, name, (meta.n_padded, 2), torch.float32)
+    return _checked(t, name, (meta.n_padded, 2), torch.float32, dev)
 
 
 def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=None,
@@ -310,19 +315,20 @@ def gather_tree_logprobs_entropy(logits, meta: TreeMeta, logprobs=None, entropy=
     [Np, 2]) receives (log-sum-exp, entropy) of every real row, which the
     backward can take instead of re-reading each row for them."""
     import torch
-    _dev_tensor(logits, "logits")
+    dev = torch.cuda.current_device()
+    _dev_tensor(logits, "logits", dev)
     if logits.dim() != 2 or logits.shape[0] != meta.n_padded:
         raise ValueError(f"logits must be [{meta.n_padded}, V], got {tuple(logits.shape)}")
     n = meta.n_out
     code = _dtype_code(logits)
     logprobs = (torch.empty(n, dtype=torch.float32, device=logits.device) if logprobs is None
-                else _checked(logprobs, "logprobs", (n,), torch.float32))
+                else _checked(logprobs, "logprobs", (n,), torch.float32, dev))
     entropy = (torch.empty(n, dtype=torch.float32, device=logits.device) if entropy is None
-               else _checked(entropy, "entropy", (n,), torch.float32))
+               else _checked(entropy, "entropy", (n,), torch.float32, dev))
     check(_lib.load().pst_gather_tree_logprobs_entropy(
         logits.data_ptr(), int(logits.shape[1]), code, meta._h,
         logprobs.data_ptr(), entropy.data_ptr(),
-        c_void_p(_ptr_or_null(_row_stats(row_stats, meta))), c_void_p(_stream_ptr(stream))))
+        c_void_p(_ptr_or_null(_row_stats(row_stats, meta, dev=dev))), c_void_p(_stream_ptr(stream))))
     return logprobs, entropy
 
 
@@ -332,18 +338,19 @@ def gather_tree_logprobs_entropy_bwd(logits, meta: TreeMeta, dlogprobs, dentropy
     dlogits [Np, V] in the logits' dtype (pad rows zero).  row_stats: the
     forward gather's row statistics for these logits (optional)."""
     import torch
-    _dev_tensor(logits, "logits")
+    dev = torch.cuda.current_device()
+    _dev_tensor(logits, "logits", dev)
     if logits.dim() != 2 or logits.shape[0] != meta.n_padded:
         raise ValueError(f"logits must be [{meta.n_padded}, V], got {tuple(logits.shape)}")
     for t, name in ((dlogprobs, "dlogprobs"), (dentropy, "dentropy")):
-        _checked(t, name, (meta.n_out,), torch.float32)
+        _checked(t, name, (meta.n_out,), torch.float32, dev)
     code = _dtype_code(logits)
     dlogits = (torch.empty_like(logits) if dlogits is None
-               else _checked(dlogits, "dlogits", logits.shape, logits.dtype))
+               else _checked(dlogits, "dlogits", logits.shape, logits.dtype, dev))
     check(_lib.load().pst_gather_tree_logprobs_entropy_bwd(
         logits.data_ptr(), int(logits.shape[1]), code, meta._h,
         dlogprobs.data_ptr(), dentropy.data_ptr(),
-        c_void_p(_ptr_or_null(_row_stats(row_stats, meta))),
+        c_void_p(_ptr_or_null(_row_stats(row_stats, meta, dev=dev))),
         dlogits.data_ptr(), c_void_p(_stream_ptr(stream))))
     return dlogits
 

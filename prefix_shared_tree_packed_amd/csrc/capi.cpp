@@ -593,8 +593,6 @@ int pst_tree_dense_mask(const pst_tree_meta* meta, int32_t format, void* out, vo
   if (!meta) return fail(PST_EINVAL, "tree metadata is NULL");
   if (format != PST_MASK_U8 && format != PST_MASK_ADD_F32 && format != PST_MASK_ADD_BF16)
     return fail(PST_EDTYPE, "unknown mask format " + std::to_string(format));
-  if (meta->dev.Np / 32 > 65535)
-    return fail(PST_ESHAPE, "Np=" + std::to_string(meta->dev.Np) + " beyond the dense-mask limit");
   if (int e = check_ptrs({out}, "out")) return e;
   if (int e = check_meta_device(meta)) return e;
   static_assert(PST_MASK_U8 == pst::kMaskU8 && PST_MASK_ADD_F32 == pst::kMaskAddF32 &&

@@ -327,15 +327,24 @@ __global__ __launch_bounds__(TPB) void gather_bwd_kernel(
   __syncthreads();
   const float lse = row_stats[0], H = row_stats[1], A = row_stats[2], B = row_stats[3];
 
-  // ---- pass 2: -p (A + B (log p + H)) for every entry
+  // ---- pass 2: -p (A + B (log p + H)) for every entry; each batch's
+  // kUnroll loads are issued before any of its stores (logits and d logits
+  // never overlap, but the compiler cannot move a load above a store to
+  // another pointer of the same type on its own), so kUnroll 16-byte reads
+  // per thread are in flight at once
   for (int64_t base = 0; base < nch; base += kUnroll * TPB) {
+    u32x4_t u[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = base + tid + j * TPB;
+      u[j] = c < nch ? __builtin_nontemporal_load(body + c) : pad;
+    }
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       const int64_t c = base + tid + j * TPB;
       if (c < nch) {
-        const u32x4_t w = body[c];
         float f[EPC], g[EPC];
-        unpack<T>(uint4{w.x, w.y, w.z, w.w}, f);
+        unpack<T>(uint4{u[j].x, u[j].y, u[j].z, u[j].w}, f);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) g[e] = grad_base(f[e], lse, H, A, B);
         const uint4 o = pack_out<T>(g);

@@ -8,7 +8,10 @@
 //
 // Each thread owns one 16-byte chunk of columns and keeps their subtree
 // ends in registers; a workgroup walks kRowsPerWg (4) rows, writing every chunk
-// once with a non-temporal store.  Write-bound: Np * Np * element bytes.
+// once with a non-temporal store.  Rows where no lane of a wave sees any of
+// its keys (above the diagonal, or past every subtree of its chunk) take the
+// constant hidden pattern without per-element tests.  Write-bound:
+// Np * Np * element bytes.
 #include "launch.h"
 
 namespace pst {
@@ -74,14 +77,29 @@ __global__ __launch_bounds__(kThreads) void dense_mask_kernel(TreeDev tr, void* 
     se[e + 2] = s.z;
     se[e + 3] = s.w;
   }
-  const int r0 = blockIdx.y * kRowsPerWg;
-  char* base = static_cast<char*>(out) + static_cast<size_t>(c0) * (16 / E);
-  for (int r = r0; r < r0 + kRowsPerWg; ++r) {
-    bool vis[E];
+  int se_max = se[0];
 #pragma unroll
-    for (int e = 0; e < E; ++e) vis[e] = c0 + e <= r && r <= se[e];
-    __builtin_nontemporal_store(MaskFmt<FMT>::pack(vis),
-                                reinterpret_cast<u32x4_t*>(base + static_cast<size_t>(r) * row_bytes));
+  for (int e = 1; e < E; ++e) se_max = max(se_max, se[e]);
+  char* base = static_cast<char*>(out) + static_cast<size_t>(c0) * (16 / E);
+  const bool none[E] = {};
+  const u32x4_t hidden = MaskFmt<FMT>::pack(none);
+  // row groups y, y + gridDim.y, ... (the grid's y extent is capped; Np is a
+  // multiple of 128, so every group is whole)
+  for (int r0 = blockIdx.y * kRowsPerWg; r0 < tr.Np; r0 += gridDim.y * kRowsPerWg)
+  for (int r = r0; r < r0 + kRowsPerWg; ++r) {
+    u32x4_t w;
+    // most of the matrix is hidden: above the diagonal (r < c0) or past
+    // every subtree of the chunk's keys; a wave whose lanes all see
+    // nothing stores the hidden pattern without the per-element tests
+    if (__all(r < c0 || r > se_max)) {
+      w = hidden;
+    } else {
+      bool vis[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) vis[e] = c0 + e <= r && r <= se[e];
+      w = MaskFmt<FMT>::pack(vis);
+    }
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(base + static_cast<size_t>(r) * row_bytes));
   }
 }
 
@@ -89,8 +107,11 @@ template <int FMT>
 hipError_t launch_fmt(const TreeDev& tr, void* out, hipStream_t stream) {
   constexpr int E = MaskFmt<FMT>::E;
   const int cols_per_wg = kThreads * E;
+  // columns in x (at most Np / 1024 workgroups for float32, well inside the
+  // x limit); row groups in y, capped at the y limit and strided over
+  const unsigned groups = static_cast<unsigned>(tr.Np / kRowsPerWg);
   const dim3 grid(static_cast<unsigned>((tr.Np + cols_per_wg - 1) / cols_per_wg),
-                  static_cast<unsigned>(tr.Np / kRowsPerWg));
+                  groups < 65535u ? groups : 65535u);
   const size_t row_bytes = static_cast<size_t>(tr.Np) * (16 / E);
   hipLaunchKernelGGL(dense_mask_kernel<FMT>, grid, dim3(kThreads), 0, stream, tr, out, row_bytes);
   return hipGetLastError();

@@ -87,30 +87,54 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T* __restrict__ x, TreeD
   }
   __syncthreads();
   // chunk c of a row: head c / (half / E), dims (c % (half / E)) * E ..
+  // A thread's chunk pairs are disjoint from every other thread's, so each
+  // batch of kBatch pairs is loaded before any of them is rotated and
+  // stored: the loads are in flight together (in place, the compiler would
+  // otherwise keep every load behind the previous pair's stores).
   const int cph = half / E;  // chunks per pair half of one head
   const int per_row = heads * cph;
-  for (int c = tid; c < kRows * per_row; c += kThreads) {
-    const int r = c / per_row;
-    const int row = row0 + r;
-    // rows past the end and pad rows (position 0: the identity) are skipped
-    if (row >= tr.Np || tr.row_out_ptr[row] == tr.row_out_ptr[row + 1]) continue;
-    const int cr = c - r * per_row;
-    const int h = cr / cph;
-    const int i0 = (cr - h * cph) * E;
-    T* xr = x + static_cast<size_t>(row) * heads * d;
-    uint4* p1 = reinterpret_cast<uint4*>(xr + h * d + i0);
-    uint4* p2 = reinterpret_cast<uint4*>(xr + h * d + half + i0);
-    float a[E], b[E], ya[E], yb[E];
-    Vec<T>::unpack(*p1, a);
-    Vec<T>::unpack(*p2, b);
+  constexpr int kBatch = 4;
+  for (int c0 = tid; c0 < kRows * per_row; c0 += kBatch * kThreads) {
+    uint4 a4[kBatch], b4[kBatch];
+    uint4* p1[kBatch];
+    uint4* p2[kBatch];
+    int rr[kBatch], ii[kBatch];
+    bool live[kBatch];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float co = cs[r][0][i0 + e], si = cs[r][1][i0 + e];
-      ya[e] = a[e] * co - b[e] * si;
-      yb[e] = b[e] * co + a[e] * si;
+    for (int j = 0; j < kBatch; ++j) {
+      const int c = c0 + j * kThreads;
+      const int row = row0 + c / per_row;
+      // rows past the end and pad rows (position 0: the identity) are skipped
+      live[j] = c < kRows * per_row && row < tr.Np && tr.row_out_ptr[row] != tr.row_out_ptr[row + 1];
+      const int cl = live[j] ? c : 0;  // a skipped slot addresses chunk 0 of row0, unused
+      const int r = cl / per_row;
+      const int cr = cl - r * per_row;
+      const int h = cr / cph;
+      rr[j] = r;
+      ii[j] = (cr - h * cph) * E;
+      T* xr = x + static_cast<size_t>(row0 + r) * heads * d;
+      p1[j] = reinterpret_cast<uint4*>(xr + h * d + ii[j]);
+      p2[j] = reinterpret_cast<uint4*>(xr + h * d + half + ii[j]);
+      if (live[j]) {
+        a4[j] = *p1[j];
+        b4[j] = *p2[j];
+      }
     }
-    *p1 = Vec<T>::pack(ya);
-    *p2 = Vec<T>::pack(yb);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (!live[j]) continue;
+      float a[E], b[E], ya[E], yb[E];
+      Vec<T>::unpack(a4[j], a);
+      Vec<T>::unpack(b4[j], b);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float co = cs[rr[j]][0][ii[j] + e], si = cs[rr[j]][1][ii[j] + e];
+        ya[e] = a[e] * co - b[e] * si;
+        yb[e] = b[e] * co + a[e] * si;
+      }
+      *p1[j] = Vec<T>::pack(ya);
+      *p2[j] = Vec<T>::pack(yb);
+    }
   }
 }
 
