@@ -311,7 +311,13 @@ int upload_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
   // dQ): grouped by their first key block, so that the blocks resident on an
   // XCD at one time share their prompt's K/V in L2, heaviest first within a
   // group (longest processing time); measured 3-4 % faster than one global
-  // heaviest-first order.  Key blocks (dK/dV): heaviest first.
+  // heaviest-first order.  Key blocks (dK/dV): grouped by the last query
+  // block that sees them (the end of their subtree), the group with the
+  // longest range first, first key block first within a group.  The dK/dV
+  // pass walks each range downwards from that end, so the workgroups of a
+  // group that are resident on an XCD read the same query rows at about the
+  // same time and share them in L2 (in a heaviest-first order they belong
+  // to unrelated subtrees, and nearly every Q / dO tile came from HBM).
   {
     std::vector<int32_t> ord(nb);
     std::iota(ord.begin(), ord.end(), 0);
@@ -325,8 +331,12 @@ int upload_meta(const std::vector<const pst::Tree*>& trees, void* stream, pst_tr
     std::copy(ord.begin(), ord.end(), h + o_ford);
     std::iota(ord.begin(), ord.end(), 0);
     const int32_t* qhi = h + o_qhi;
+    std::vector<int32_t> span(nb, 0);  // per range end: the longest range ending there
+    for (int32_t b = 0; b < nb; ++b) span[qhi[b]] = std::max(span[qhi[b]], qhi[b] - b + 1);
     std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
-      return qhi[a] - a > qhi[b] - b;
+      if (span[qhi[a]] != span[qhi[b]]) return span[qhi[a]] > span[qhi[b]];
+      if (qhi[a] != qhi[b]) return qhi[a] < qhi[b];
+      return a < b;
     });
     std::copy(ord.begin(), ord.end(), h + o_bord);
     // 32-query units: the same grouping by first key block, most blocks first

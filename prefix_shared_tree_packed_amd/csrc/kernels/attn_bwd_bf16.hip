@@ -166,19 +166,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   const int qhi = cst(tr.kb_qhi)[kb];
   const int n_steps = (qhi - kb + 1) * G * 2;
   // step -> (query block, head of the group, half): steps walk halves, then
-  // heads, then blocks; cursors advance one step at a time
+  // heads, then blocks from qhi down to kb (the key blocks sharing qhi run
+  // side by side and read the same query rows at about the same time);
+  // cursors advance one step at a time
   struct Cursor {
     int qb, r, half;
   };
   auto cursor_at = [&](int st) {
     const int rest = st >> 1;
-    return Cursor{kb + rest / G, rest % G, st & 1};
+    return Cursor{qhi - rest / G, rest % G, st & 1};
   };
   auto advance = [&](Cursor& cu) {
     cu.half ^= 1;
     if (cu.half == 0 && ++cu.r == G) {
       cu.r = 0;
-      ++cu.qb;
+      --cu.qb;
     }
   };
   auto decode = [&](const Cursor& cu, int& h, int& q0) {

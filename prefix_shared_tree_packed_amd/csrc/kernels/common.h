@@ -27,8 +27,8 @@ struct TreeDev {
   const int32_t* q_ptr;        // [nb+1] tiles of each query block
   const int32_t* q_tile;       // [n_tiles] (key block << 1) | full
   const int32_t* kb_qhi;       // [nb] last query block seeing each key block
-  const int32_t* fwd_order;    // [nb] query blocks, heaviest first
-  const int32_t* bwd_order;    // [nb] key blocks, heaviest first
+  const int32_t* fwd_order;    // [nb] query blocks by first key block, heaviest first
+  const int32_t* bwd_order;    // [nb] key blocks by range end, longest range first
   const int32_t* row_out_ptr;  // [Np+1] outputs of each row (none for pad rows)
   const int32_t* out_pos;      // [n_out] output slot
   const int32_t* out_tgt;      // [n_out] next-token id, -1 for a last token
