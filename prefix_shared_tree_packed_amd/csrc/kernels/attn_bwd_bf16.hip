@@ -63,12 +63,12 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 // --------------------------------------------------------------------- dK, dV
-// A wave owns 32 keys (two 16-key halves kh) of one key/value head and walks
-// every visible query block of the G query heads in 64-query steps (three
-// stages of LDS, one workgroup per CU).  All products are 16x16x32 MFMAs:
-// per 32-query slice, S = Q.K^T and dP = dO.V^T are eight independent
-// 16x16 chains, and dV^T += dO^T.P, dK^T += Q^T.dS sixteen independent
-// blocks each, so one wave per SIMD keeps the matrix core busy.
+// A pair of waves owns 32 keys (two 16-key halves kh) of one key/value head
+// and walks every visible query block of the G query heads in 64-query
+// steps (three stages of LDS, one workgroup per CU).  All products are
+// 16x16x32 MFMAs: per 32-query slice, S = Q.K^T and dP = dO.V^T are eight
+// independent 16x16 chains, and dV^T += dO^T.P, dK^T += Q^T.dS sixteen
+// independent blocks each.
 constexpr int kKvStep = 64;                 // queries per step
 constexpr int kKvBuf = kKvStep * kRowB;     // 16 KB
 constexpr int kHalf16 = 16 * kRowB;         // byte offset of rows 16..31 of a 32-row slice
@@ -101,16 +101,20 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x4_t& lo, const f32x4_t& hi) 
 // 128 kb + 32 p).  Wave p (role A) computes S = Q.K^T, masks it, forms
 // P = exp(S c - LSE) and accumulates dV^T += dO^T.P; it hands P (bf16, in
 // its accumulator layout) to wave p + 4 (role B) through LDS.  B computes
-// dP = dO.V^T (accumulators starting at -D) and, one 32-query sub-block
-// behind A, dS = P (dP - D) and dK^T += Q^T.dS.  Each wave holds one
-// accumulator set and one of K, V, so two waves share a SIMD and one's
-// exponentials run beside the other's MFMAs.  Every wave passes the same
-// barriers: two per 64-query step (at each 32-query sub-block; the first
-// also waits for the step's tiles), one after the loop for B's last
-// sub-block.  Four tile stages: B reads the previous sub-block's Q while
-// the step after next streams in.
-constexpr int kKvStages = 4;
+// dP = dO.V^T (accumulators starting at -D) and, one 64-query step behind
+// A, dS = P (dP - D) and dK^T += Q^T.dS.  Each wave holds one accumulator
+// set and one of K, V, so two waves share a SIMD.  A software-pipelines the
+// two 32-query sub-blocks of a step: the first sub-block's exponentials
+// issue between the MFMAs of the second's S, the second's between those of
+// the first's dV, so its VALU work runs beside the matrix core (measured
+// 3 % faster than sub-blocks in turn; the same for B's dS cost 1.5 %).
+// Every wave passes one barrier per step (which also waits for the step's
+// tiles) and one after the loop for B's last step.  Three tile stages:
+// while a step computes, B reads the previous step's Q and the next step
+// streams in.
+constexpr int kKvStages = 3;
 constexpr int kPexB = 2 * 1024;  // one pair's P of one sub-block: 2 chunks x 64 lanes x 16 B
+constexpr int kPexSlots = 4;     // two steps of two 32-query sub-blocks
 
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -122,9 +126,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageB];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageB];
   __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageB];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage3[kStageB];
-  // P handed from A to B: [pair][sub-block parity][chunk kh][lane] x 16 B
-  __shared__ __attribute__((aligned(1024))) uint8_t pex[4 * 2 * kPexB];
+  // P handed from A to B: [pair][slot: step parity x half][chunk kh][lane] x 16 B
+  __shared__ __attribute__((aligned(1024))) uint8_t pex[4 * kPexSlots * kPexB];
 
   const int G = hq / hkv;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   f32x4_t acc[8][2];  // (d block db, key half kh): dV^T (A) or dK^T (B)
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc[db][0] = acc[db][1] = f32x4_t{};
-  f32x4_t dpacc[2][2];  // B: dP - D of the sub-block it finishes next (query half q16, key half kh)
+  f32x4_t dpacc[2][2][2];  // B: dP - D of the step it finishes next (32-query half, q16, kh)
 
   const uint32_t q_bytes = static_cast<uint32_t>(hq) * D * 2;  // one token's Q (or dO) rows
   const int qhi = cst(tr.kb_qhi)[kb];
@@ -187,11 +190,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     h = g * G + cu.r;
     q0 = cu.qb * kTile + kKvStep * cu.half;
   };
-  // Every wave issues kDmaOps tile DMA instructions per step; waves 0 and 1
-  // also one for LSE / D, first, so a wait for vmcnt(kDmaOps) lands every
-  // step but the newest.
+  // all eight waves share each step's tile DMA
   constexpr int kNw = 8;
-  constexpr int kDmaOps = 2 * TileOff<kKvStep, kNw>::kOps;
   const TileOff<kKvStep, kNw> qoff = tile_offsets<kKvStep, kNw>(q_bytes, wave, lane);
   auto issue_loads = [&](const Cursor& cu, uint8_t* stg) {
     int h, q0;
@@ -207,19 +207,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     dma_tile_s<kKvStep, kNw>(reinterpret_cast<const char*>(dout) + row0, qoff, base + kStDo, wave);
   };
   auto empty_at = [&](int qlo) { return kbase > qlo + 31 || smax < qlo; };
-  uint8_t* const pex_pair = pex + pair * (2 * kPexB);
+  uint8_t* const pex_pair = pex + pair * (kPexSlots * kPexB);
+  // A operand reads of fragment f (d slice f / 2, query half f % 2) of a slice
+  auto qoffs = [&](int f) { return ((f & 1) ? kHalf16 : 0) + roff[f >> 1]; };
 
-  // A: sub-block (stage stg, 32-query half qs at query qlo): S, mask, P,
-  // dV; P goes to pex slot `slot`
-  auto run_a = [&](const uint8_t* stg, int qs, int qlo, int slot) {
-    const bool full = kbase + 31 <= qlo && smin >= qlo + 31;
+  // A's pieces for one 32-query sub-block (half qs of a stage, first query
+  // qlo).  S = Q.K^T: eight independent 16x16 chains.
+  auto a_scores = [&](const uint8_t* stg, int qs, f32x4_t (&sacc)[2][2]) {
     const uint8_t* qsl = stg + 32 * qs * kRowB;
-    const uint8_t* dosl = stg + kStDo + 32 * qs * kRowB;
-    const float* lsl = reinterpret_cast<const float*>(stg + kStLs);
-    f32x4_t sacc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a) sacc[a][0] = sacc[a][1] = f32x4_t{};
-    auto qoffs = [&](int f) { return ((f & 1) ? kHalf16 : 0) + roff[f >> 1]; };
     bf16x8_t qbuf[3];
     qbuf[0] = lds_frag(qsl, qoffs(0));
     qbuf[1] = lds_frag(qsl, qoffs(1));
@@ -231,36 +228,55 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) sacc[q16][kh] = mma16(qbuf[f % 3], kvf[kh][s4], sacc[q16][kh]);
     }
-    // register i of block (q16, kh) is query qlo + 16 q16 + 4 lg + i, key
-    // kbase + 16 kh + li; key j sees query q iff (unsigned)(q - j) <= se[j] - j
-    if (!full) {
-      const int A = qlo + 4 * lg - kbase - li;
+  };
+  // register i of block (q16, kh) is query qlo + 16 q16 + 4 lg + i, key
+  // kbase + 16 kh + li; key j sees query q iff (unsigned)(q - j) <= se[j] - j.
+  // A sub-block every pair of which is visible skips the test.
+  auto a_mask = [&](f32x4_t (&sacc)[2][2], int qlo) {
+    if (kbase + 31 <= qlo && smin >= qlo + 31) return;
+    const int A = qlo + 4 * lg - kbase - li;
 #pragma unroll
-      for (int q16 = 0; q16 < 2; ++q16)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t dlt = static_cast<uint32_t>(A + 16 * q16 + i - 16 * kh);
-            sacc[q16][kh][i] = dlt <= static_cast<uint32_t>(span_k[kh]) ? sacc[q16][kh][i] : -INFINITY;
-          }
-    }
-#pragma unroll
-    for (int q16 = 0; q16 < 2; ++q16) {
-      const float4 l4 = *reinterpret_cast<const float4*>(lsl + 32 * qs + 16 * q16 + 4 * lg);
-      const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+    for (int q16 = 0; q16 < 2; ++q16)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[q16][kh][i] = fast_exp2(fmaf(sacc[q16][kh][i], c, -lv[i]));
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t dlt = static_cast<uint32_t>(A + 16 * q16 + i - 16 * kh);
+          sacc[q16][kh][i] = dlt <= static_cast<uint32_t>(span_k[kh]) ? sacc[q16][kh][i] : -INFINITY;
+        }
+  };
+  // the rows' LSE in the exp2 domain: lv[q16][i] for query 16 q16 + 4 lg + i
+  auto a_lse = [&](const uint8_t* stg, int qs, float (&lv)[2][4]) {
+    const float* lsl = reinterpret_cast<const float*>(stg + kStLs);
+#pragma unroll
+    for (int q16 = 0; q16 < 2; ++q16) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lsl + 32 * qs + 16 * q16 + 4 * lg);
+      lv[q16][0] = l4.x * kLog2e;
+      lv[q16][1] = l4.y * kLog2e;
+      lv[q16][2] = l4.z * kLog2e;
+      lv[q16][3] = l4.w * kLog2e;
     }
-    bf16x8_t pf[2];
+  };
+  // P = exp2(S c - LSE) of element e (q16 = e / 8, kh = e / 4 % 2, i = e % 4)
+  auto a_exp = [&](f32x4_t (&sacc)[2][2], const float (&lv)[2][4], int e) {
+    const int q16 = e >> 3, kh = (e >> 2) & 1, i = e & 3;
+    sacc[q16][kh][i] = fast_exp2(fmaf(sacc[q16][kh][i], c, -lv[q16][i]));
+  };
+  // P to bf16 (B operands of dV^T += dO^T.P), and to pex slot `slot` for B
+  auto a_pack = [&](const f32x4_t (&sacc)[2][2], int slot, bf16x8_t (&pf)[2]) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       pf[kh] = pack8(sacc[0][kh], sacc[1][kh]);
       *reinterpret_cast<bf16x8_t*>(pex_pair + slot * kPexB + kh * 1024 + lane * 16) = pf[kh];
     }
-    // dV^T += dO^T.P; transposed reads two d blocks ahead
+  };
+  // dV^T += dO^T.P of half qs, transposed reads two d blocks ahead; with
+  // kNext, the exponentials of the next sub-block's scores `nxt` issue
+  // between the MFMAs, two per d block
+  auto a_dv = [&](auto next, const uint8_t* stg, int qs, const bf16x8_t (&pf)[2],
+                  f32x4_t (&nxt)[2][2], const float (&nlv)[2][4]) {
+    constexpr bool kNext = decltype(next)::value;
+    const uint8_t* dosl = stg + kStDo + 32 * qs * kRowB;
     bf16x8_t obuf[3];
     obuf[0] = lds_t16_frag(dosl, trv, 0);
     obuf[1] = lds_t16_frag(dosl, trv, 1);
@@ -268,11 +284,62 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     for (int db = 0; db < 8; ++db) {
       if (db + 2 < 8) obuf[(db + 2) % 3] = lds_t16_frag(dosl, trv, db + 2);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) acc[db][kh] = mma16(obuf[db % 3], pf[kh], acc[db][kh]);
+      acc[db][0] = mma16(obuf[db % 3], pf[0], acc[db][0]);
+      if constexpr (kNext) a_exp(nxt, nlv, 2 * db);
+      acc[db][1] = mma16(obuf[db % 3], pf[1], acc[db][1]);
+      if constexpr (kNext) a_exp(nxt, nlv, 2 * db + 1);
     }
   };
-  // B, first half of its work on a sub-block: dP - D into dpacc
+  // A on one sub-block: S, mask, P, dV
+  auto run_a = [&](const uint8_t* stg, int qs, int qlo, int slot) {
+    f32x4_t sacc[2][2];
+    a_scores(stg, qs, sacc);
+    a_mask(sacc, qlo);
+    float lv[2][4];
+    a_lse(stg, qs, lv);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a_exp(sacc, lv, e);
+    bf16x8_t pf[2];
+    a_pack(sacc, slot, pf);
+    a_dv(std::false_type{}, stg, qs, pf, sacc, lv);
+  };
+  // A on both sub-blocks of a step, software-pipelined: the first
+  // sub-block's exponentials issue between the second's S MFMAs, the
+  // second's between the first's dV MFMAs, so the VALU work runs beside
+  // the matrix core rather than between this wave's MFMA phases
+  auto run_a2 = [&](const uint8_t* stg, int q0, int par) {
+    f32x4_t s0[2][2], s1[2][2];
+    float lv0[2][4], lv1[2][4];
+    a_scores(stg, 0, s0);
+    a_mask(s0, q0);
+    a_lse(stg, 0, lv0);
+    {  // S of the second sub-block with P of the first
+      const uint8_t* qsl = stg + 32 * kRowB;
+#pragma unroll
+      for (int a = 0; a < 2; ++a) s1[a][0] = s1[a][1] = f32x4_t{};
+      bf16x8_t qbuf[3];
+      qbuf[0] = lds_frag(qsl, qoffs(0));
+      qbuf[1] = lds_frag(qsl, qoffs(1));
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+        if (f + 2 < 8) qbuf[(f + 2) % 3] = lds_frag(qsl, qoffs(f + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        const int s4 = f >> 1, q16 = f & 1;
+        s1[q16][0] = mma16(qbuf[f % 3], kvf[0][s4], s1[q16][0]);
+        a_exp(s0, lv0, 2 * f);
+        s1[q16][1] = mma16(qbuf[f % 3], kvf[1][s4], s1[q16][1]);
+        a_exp(s0, lv0, 2 * f + 1);
+      }
+    }
+    bf16x8_t pf0[2], pf1[2];
+    a_pack(s0, 2 * par, pf0);
+    a_mask(s1, q0 + 32);
+    a_lse(stg, 1, lv1);
+    a_dv(std::true_type{}, stg, 0, pf0, s1, lv1);
+    a_pack(s1, 2 * par + 1, pf1);
+    a_dv(std::false_type{}, stg, 1, pf1, s1, lv1);
+  };
+  // B, first half of its work on a sub-block: dP - D into dpacc[qs]
   auto run_b_dp = [&](const uint8_t* stg, int qs) {
     const uint8_t* dosl = stg + kStDo + 32 * qs * kRowB;
     const float* ddl = reinterpret_cast<const float*>(stg + kStDd);
@@ -280,9 +347,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     for (int a = 0; a < 2; ++a) {
       const float4 d4 = *reinterpret_cast<const float4*>(ddl + 32 * qs + 16 * a + 4 * lg);
       const f32x4_t negd = {-d4.x, -d4.y, -d4.z, -d4.w};
-      dpacc[a][0] = dpacc[a][1] = negd;
+      dpacc[qs][a][0] = dpacc[qs][a][1] = negd;
     }
-    auto qoffs = [&](int f) { return ((f & 1) ? kHalf16 : 0) + roff[f >> 1]; };
     bf16x8_t dbuf[3];
     dbuf[0] = lds_frag(dosl, qoffs(0));
     dbuf[1] = lds_frag(dosl, qoffs(1));
@@ -292,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
       __builtin_amdgcn_sched_barrier(0);
       const int s4 = f >> 1, q16 = f & 1;
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) dpacc[q16][kh] = mma16(dbuf[f % 3], kvf[kh][s4], dpacc[q16][kh]);
+      for (int kh = 0; kh < 2; ++kh) dpacc[qs][q16][kh] = mma16(dbuf[f % 3], kvf[kh][s4], dpacc[qs][q16][kh]);
     }
   };
   // B, second half: dS = P (dP - D) with A's P from pex slot `slot`, dK^T += Q^T.dS
@@ -306,10 +372,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
       f32x4_t lo, hi;  // dS of query halves 0 and 1 (P in slots 0..3, 4..7)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        lo[2 * i] = __uint_as_float(w[i] << 16) * dpacc[0][kh][2 * i];
-        lo[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * dpacc[0][kh][2 * i + 1];
-        hi[2 * i] = __uint_as_float(w[2 + i] << 16) * dpacc[1][kh][2 * i];
-        hi[2 * i + 1] = __uint_as_float(w[2 + i] & 0xffff0000u) * dpacc[1][kh][2 * i + 1];
+        lo[2 * i] = __uint_as_float(w[i] << 16) * dpacc[qs][0][kh][2 * i];
+        lo[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * dpacc[qs][0][kh][2 * i + 1];
+        hi[2 * i] = __uint_as_float(w[2 + i] << 16) * dpacc[qs][1][kh][2 * i];
+        hi[2 * i + 1] = __uint_as_float(w[2 + i] & 0xffff0000u) * dpacc[qs][1][kh][2 * i + 1];
       }
       sf[kh] = pack8(lo, hi);
     }
@@ -325,13 +391,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     }
   };
 
-  // the first two steps' tiles start streaming, then the K/V rows and
-  // subtree ends load beside them and complete here (empty asm uses pin
-  // them before the loop: the compiler does not count the assembly DMA, so
-  // its own waits for these loads, left inside the loop, would drain the
-  // prefetch)
+  // the first step's tiles start streaming, then the K/V rows and subtree
+  // ends load beside them and complete here (empty asm uses pin them before
+  // the loop: the compiler does not count the assembly DMA, so its own
+  // waits for these loads, left inside the loop, would drain the prefetch)
   issue_loads(cursor_at(0), stage0);
-  issue_loads(cursor_at(1), stage1);  // n_steps >= 2
   {
     const bf16_t* src = roleA ? k : v;
 #pragma unroll
@@ -356,51 +420,59 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   // come from).
   auto loop = [&](auto role) {
     constexpr bool kA = decltype(role)::value;
-    Cursor cur = cursor_at(0), pf = cursor_at(n_steps > 2 ? 2 : n_steps - 1);
-    // B's pending sub-block: its stage, half, and whether it has any pair
+    Cursor cur = cursor_at(0), pf = cursor_at(1);  // n_steps >= 2
+    // B's pending step: its stage, and which of its halves have any pair
     const uint8_t* pend_stg = stage0;
-    int pend_qs = 0;
-    bool pend_live = false;
+    int pend_par = 0;
+    bool pend_live[2] = {false, false};
     auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
       int h, q0;
       decode(cur, h, q0);
       advance(cur);
+      // step st staged, the previous step's P written and LDS reads done;
+      // then step st + 1 streams into the stage step st - 2 used (B finished
+      // with it during step st - 1)
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (st + 1 < n_steps) {
+        issue_loads(pf, fill);
+        advance(pf);
+      }
+      const int par = st & 1;
+      bool live[2];
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        if (qs == 0) {
-          // step st staged by every wave, the previous sub-block's P and
-          // LDS reads done; then prefetch step min(st + 2, n_steps - 1) into
-          // the stage step st - 2 used (free: B finished with it a step ago)
-          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaOps) : "memory");
-          issue_loads(pf, fill);
-          if (st + 3 < n_steps) advance(pf);
+      for (int qs = 0; qs < 2; ++qs) live[qs] = !empty_at(q0 + 32 * qs);
+      if constexpr (kA) {
+        if (live[0] && live[1]) {
+          run_a2(stg, q0, par);
         } else {
-          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs)
+            if (live[qs]) run_a(stg, qs, q0 + 32 * qs, 2 * par + qs);
         }
-        const int qlo = q0 + 32 * qs;
-        const bool live = !empty_at(qlo);
-        if constexpr (kA) {
-          if (live) run_a(stg, qs, qlo, qs);
-        } else {
-          // each sub-block's P sits in the pex slot of its own half
-          if (pend_live) run_b_dk(pend_stg, pend_qs, pend_qs);
-          if (live) run_b_dp(stg, qs);
-          pend_stg = stg;
-          pend_qs = qs;
-          pend_live = live;
-        }
+      } else {
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+          if (pend_live[qs]) run_b_dk(pend_stg, qs, 2 * pend_par + qs);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+          if (live[qs]) run_b_dp(stg, qs);
+        pend_stg = stg;
+        pend_par = par;
+        pend_live[0] = live[0];
+        pend_live[1] = live[1];
       }
     };
-    for (int st = 0; st < n_steps; st += kKvStages) {  // four-stage ring: step st uses stage st % 4
-      step(st, stage0, stage2);
-      if (st + 1 < n_steps) step(st + 1, stage1, stage3);
+    for (int st = 0; st < n_steps; st += kKvStages) {  // three-stage ring: step st uses stage st % 3
+      step(st, stage0, stage1);
+      if (st + 1 < n_steps) step(st + 1, stage1, stage2);
       if (st + 2 < n_steps) step(st + 2, stage2, stage0);
-      if (st + 3 < n_steps) step(st + 3, stage3, stage1);
     }
-    // B's last sub-block
+    // B's last step
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (!kA) {
-      if (pend_live) run_b_dk(pend_stg, pend_qs, pend_qs);
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+        if (pend_live[qs]) run_b_dk(pend_stg, qs, 2 * pend_par + qs);
     }
   };
   if (roleA)
