@@ -120,7 +120,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dsum,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, TreeDev tr, int hq, int hkv, float c,
-    float scale) {
+    float scale, int lanes, int lanes_log2) {
   // one named array per stage, so the compiler tells the in-flight DMA
   // target from the stage being read
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageB];
@@ -130,9 +130,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   __shared__ __attribute__((aligned(1024))) uint8_t pex[4 * kPexSlots * kPexB];
 
   const int G = hq / hkv;
+  // persistent: `lanes` workgroups per key/value group, each walking the
+  // key blocks the host's list scheduling dealt to its lane
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int g = logical / tr.nb;
-  const int kb = cst(tr.bwd_order)[logical - g * tr.nb];
+  const int g = logical / lanes;
+  const int lane_id = logical - g * lanes;
+  cint32* lane_ptr = cst(tr.bwd_lanes) + (lanes - 1) + lanes_log2 + lanes_log2 * tr.nb;
+  const int it0 = lane_ptr[lane_id], it1 = lane_ptr[lane_id + 1];
+  cint32* lane_items = lane_ptr + lanes + 1;
+  // the current key block and its per-block state (set for each block below)
+  int kb = 0, kbase = 0, smin = 0, smax = 0, qhi = 0, n_steps = 0;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -141,16 +148,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   const bool roleA = wave < 4;  // wave-uniform
   const int li = lane % 16;     // key column of the 16x16 blocks
   const int lg = lane / 16;     // 16-lane group: queries 4 lg .. 4 lg + 3 of each block
-  const int kbase = kb * kTile + 32 * pair;  // first key of this pair
   int span_k[2];  // se - key of this lane's key in each half (A); loaded below
   cint32* blk32 = cst(tr.blk32);
-  const int smin = blk32[2 * (kbase >> 5)], smax = blk32[2 * (kbase >> 5) + 1];
   // B operands: K^T (A) or V^T (B), key kbase + 16 kh + li, d = 32 s + 8 lg
   // .. +7; loaded below, once the first tiles are on their way
   bf16x8_t kvf[2][4];
   // A operands Q / dO: query row li of a 16-row block, chunk 4 s + lg
   int roff[4];
-#pragma unroll
+  #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) roff[s4] = li * kRowB + (((4 * s4 + lg) ^ rsw(li)) << 4);
   // transposed reads: lane i of group lg addresses token 4 lg + i / 4 at d = 4 (i % 4) .. +3
   int trv;
@@ -161,13 +166,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   }
 
   f32x4_t acc[8][2];  // (d block db, key half kh): dV^T (A) or dK^T (B)
-#pragma unroll
-  for (int db = 0; db < 8; ++db) acc[db][0] = acc[db][1] = f32x4_t{};
   f32x4_t dpacc[2][2][2];  // B: dP - D of the step it finishes next (32-query half, q16, kh)
 
   const uint32_t q_bytes = static_cast<uint32_t>(hq) * D * 2;  // one token's Q (or dO) rows
-  const int qhi = cst(tr.kb_qhi)[kb];
-  const int n_steps = (qhi - kb + 1) * G * 2;
   // step -> (query block, head of the group, half): steps walk halves, then
   // heads, then blocks from qhi down to kb (the key blocks sharing qhi run
   // side by side and read the same query rows at about the same time);
@@ -215,17 +216,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   // qlo).  S = Q.K^T: eight independent 16x16 chains.
   auto a_scores = [&](const uint8_t* stg, int qs, f32x4_t (&sacc)[2][2]) {
     const uint8_t* qsl = stg + 32 * qs * kRowB;
-#pragma unroll
+    #pragma unroll
     for (int a = 0; a < 2; ++a) sacc[a][0] = sacc[a][1] = f32x4_t{};
     bf16x8_t qbuf[3];
     qbuf[0] = lds_frag(qsl, qoffs(0));
     qbuf[1] = lds_frag(qsl, qoffs(1));
-#pragma unroll
+    #pragma unroll
     for (int f = 0; f < 8; ++f) {
       if (f + 2 < 8) qbuf[(f + 2) % 3] = lds_frag(qsl, qoffs(f + 2));
       __builtin_amdgcn_sched_barrier(0);
       const int s4 = f >> 1, q16 = f & 1;
-#pragma unroll
+      #pragma unroll
       for (int kh = 0; kh < 2; ++kh) sacc[q16][kh] = mma16(qbuf[f % 3], kvf[kh][s4], sacc[q16][kh]);
     }
   };
@@ -235,11 +236,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   auto a_mask = [&](f32x4_t (&sacc)[2][2], int qlo) {
     if (kbase + 31 <= qlo && smin >= qlo + 31) return;
     const int A = qlo + 4 * lg - kbase - li;
-#pragma unroll
+    #pragma unroll
     for (int q16 = 0; q16 < 2; ++q16)
-#pragma unroll
+      #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
+        #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t dlt = static_cast<uint32_t>(A + 16 * q16 + i - 16 * kh);
           sacc[q16][kh][i] = dlt <= static_cast<uint32_t>(span_k[kh]) ? sacc[q16][kh][i] : -INFINITY;
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   // the rows' LSE in the exp2 domain: lv[q16][i] for query 16 q16 + 4 lg + i
   auto a_lse = [&](const uint8_t* stg, int qs, float (&lv)[2][4]) {
     const float* lsl = reinterpret_cast<const float*>(stg + kStLs);
-#pragma unroll
+    #pragma unroll
     for (int q16 = 0; q16 < 2; ++q16) {
       const float4 l4 = *reinterpret_cast<const float4*>(lsl + 32 * qs + 16 * q16 + 4 * lg);
       lv[q16][0] = l4.x * kLog2e;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   };
   // P to bf16 (B operands of dV^T += dO^T.P), and to pex slot `slot` for B
   auto a_pack = [&](const f32x4_t (&sacc)[2][2], int slot, bf16x8_t (&pf)[2]) {
-#pragma unroll
+    #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       pf[kh] = pack8(sacc[0][kh], sacc[1][kh]);
       *reinterpret_cast<bf16x8_t*>(pex_pair + slot * kPexB + kh * 1024 + lane * 16) = pf[kh];
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     bf16x8_t obuf[3];
     obuf[0] = lds_t16_frag(dosl, trv, 0);
     obuf[1] = lds_t16_frag(dosl, trv, 1);
-#pragma unroll
+    #pragma unroll
     for (int db = 0; db < 8; ++db) {
       if (db + 2 < 8) obuf[(db + 2) % 3] = lds_t16_frag(dosl, trv, db + 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     a_mask(sacc, qlo);
     float lv[2][4];
     a_lse(stg, qs, lv);
-#pragma unroll
+    #pragma unroll
     for (int e = 0; e < 16; ++e) a_exp(sacc, lv, e);
     bf16x8_t pf[2];
     a_pack(sacc, slot, pf);
@@ -315,12 +316,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     a_lse(stg, 0, lv0);
     {  // S of the second sub-block with P of the first
       const uint8_t* qsl = stg + 32 * kRowB;
-#pragma unroll
+      #pragma unroll
       for (int a = 0; a < 2; ++a) s1[a][0] = s1[a][1] = f32x4_t{};
       bf16x8_t qbuf[3];
       qbuf[0] = lds_frag(qsl, qoffs(0));
       qbuf[1] = lds_frag(qsl, qoffs(1));
-#pragma unroll
+      #pragma unroll
       for (int f = 0; f < 8; ++f) {
         if (f + 2 < 8) qbuf[(f + 2) % 3] = lds_frag(qsl, qoffs(f + 2));
         __builtin_amdgcn_sched_barrier(0);
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   auto run_b_dp = [&](const uint8_t* stg, int qs) {
     const uint8_t* dosl = stg + kStDo + 32 * qs * kRowB;
     const float* ddl = reinterpret_cast<const float*>(stg + kStDd);
-#pragma unroll
+    #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const float4 d4 = *reinterpret_cast<const float4*>(ddl + 32 * qs + 16 * a + 4 * lg);
       const f32x4_t negd = {-d4.x, -d4.y, -d4.z, -d4.w};
@@ -352,12 +353,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     bf16x8_t dbuf[3];
     dbuf[0] = lds_frag(dosl, qoffs(0));
     dbuf[1] = lds_frag(dosl, qoffs(1));
-#pragma unroll
+    #pragma unroll
     for (int f = 0; f < 8; ++f) {
       if (f + 2 < 8) dbuf[(f + 2) % 3] = lds_frag(dosl, qoffs(f + 2));
       __builtin_amdgcn_sched_barrier(0);
       const int s4 = f >> 1, q16 = f & 1;
-#pragma unroll
+      #pragma unroll
       for (int kh = 0; kh < 2; ++kh) dpacc[qs][q16][kh] = mma16(dbuf[f % 3], kvf[kh][s4], dpacc[qs][q16][kh]);
     }
   };
@@ -365,12 +366,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
   auto run_b_dk = [&](const uint8_t* stg, int qs, int slot) {
     const uint8_t* qsl = stg + 32 * qs * kRowB;
     bf16x8_t sf[2];
-#pragma unroll
+    #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       const uint4 pw = *reinterpret_cast<const uint4*>(pex_pair + slot * kPexB + kh * 1024 + lane * 16);
       const uint32_t w[4] = {pw.x, pw.y, pw.z, pw.w};
       f32x4_t lo, hi;  // dS of query halves 0 and 1 (P in slots 0..3, 4..7)
-#pragma unroll
+      #pragma unroll
       for (int i = 0; i < 2; ++i) {
         lo[2 * i] = __uint_as_float(w[i] << 16) * dpacc[qs][0][kh][2 * i];
         lo[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * dpacc[qs][0][kh][2 * i + 1];
@@ -382,115 +383,127 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(
     bf16x8_t tbuf[3];
     tbuf[0] = lds_t16_frag(qsl, trv, 0);
     tbuf[1] = lds_t16_frag(qsl, trv, 1);
-#pragma unroll
+    #pragma unroll
     for (int db = 0; db < 8; ++db) {
       if (db + 2 < 8) tbuf[(db + 2) % 3] = lds_t16_frag(qsl, trv, db + 2);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
+      #pragma unroll
       for (int kh = 0; kh < 2; ++kh) acc[db][kh] = mma16(tbuf[db % 3], sf[kh], acc[db][kh]);
     }
   };
 
-  // the first step's tiles start streaming, then the K/V rows and subtree
-  // ends load beside them and complete here (empty asm uses pin them before
-  // the loop: the compiler does not count the assembly DMA, so its own
-  // waits for these loads, left inside the loop, would drain the prefetch)
-  issue_loads(cursor_at(0), stage0);
-  {
-    const bf16_t* src = roleA ? k : v;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      span_k[kh] = tr.se[kbase + 16 * kh + li] - (kbase + 16 * kh + li);
-      const size_t off = (static_cast<size_t>(kbase + 16 * kh + li) * hkv + g) * D + 8 * lg;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        kvf[kh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + off + 32 * s4));
-    }
-  }
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    asm volatile("" ::"v"(span_k[kh]));
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) asm volatile("" ::"v"(kvf[kh][s4]));
-  }
-
-  // The step loop, instantiated once per role so that neither role's
-  // registers flow through the other's branches; both pass the same
-  // barriers in the same order (s_barrier counts arrivals, wherever they
-  // come from).
-  auto loop = [&](auto role) {
-    constexpr bool kA = decltype(role)::value;
-    Cursor cur = cursor_at(0), pf = cursor_at(1);  // n_steps >= 2
-    // B's pending step: its stage, and which of its halves have any pair
-    const uint8_t* pend_stg = stage0;
-    int pend_par = 0;
-    bool pend_live[2] = {false, false};
-    auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
-      int h, q0;
-      decode(cur, h, q0);
-      advance(cur);
-      // step st staged, the previous step's P written and LDS reads done;
-      // then step st + 1 streams into the stage step st - 2 used (B finished
-      // with it during step st - 1)
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (st + 1 < n_steps) {
-        issue_loads(pf, fill);
-        advance(pf);
+  for (int it = it0; it < it1; ++it) {
+    kb = lane_items[it];
+    kbase = kb * kTile + 32 * pair;  // first key of this pair
+    smin = blk32[2 * (kbase >> 5)];
+    smax = blk32[2 * (kbase >> 5) + 1];
+    qhi = cst(tr.kb_qhi)[kb];
+    n_steps = (qhi - kb + 1) * G * 2;
+    #pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db][0] = acc[db][1] = f32x4_t{};
+    // the previous block's LDS reads are done before its stages refill
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the first step's tiles start streaming, then the K/V rows and subtree
+    // ends load beside them and complete here (empty asm uses pin them before
+    // the loop: the compiler does not count the assembly DMA, so its own
+    // waits for these loads, left inside the loop, would drain the prefetch)
+    issue_loads(cursor_at(0), stage0);
+    {
+      const bf16_t* src = roleA ? k : v;
+      #pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        span_k[kh] = tr.se[kbase + 16 * kh + li] - (kbase + 16 * kh + li);
+        const size_t off = (static_cast<size_t>(kbase + 16 * kh + li) * hkv + g) * D + 8 * lg;
+        #pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          kvf[kh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + off + 32 * s4));
       }
-      const int par = st & 1;
-      bool live[2];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) live[qs] = !empty_at(q0 + 32 * qs);
-      if constexpr (kA) {
-        if (live[0] && live[1]) {
-          run_a2(stg, q0, par);
-        } else {
-#pragma unroll
-          for (int qs = 0; qs < 2; ++qs)
-            if (live[qs]) run_a(stg, qs, q0 + 32 * qs, 2 * par + qs);
+    }
+    #pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      asm volatile("" ::"v"(span_k[kh]));
+      #pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) asm volatile("" ::"v"(kvf[kh][s4]));
+    }
+
+    // The step loop, instantiated once per role so that neither role's
+    // registers flow through the other's branches; both pass the same
+    // barriers in the same order (s_barrier counts arrivals, wherever they
+    // come from).
+    auto loop = [&](auto role) {
+      constexpr bool kA = decltype(role)::value;
+      Cursor cur = cursor_at(0), pf = cursor_at(1);  // n_steps >= 2
+      // B's pending step: its stage, and which of its halves have any pair
+      const uint8_t* pend_stg = stage0;
+      int pend_par = 0;
+      bool pend_live[2] = {false, false};
+      auto step = [&](int st, const uint8_t* stg, uint8_t* fill) {
+        int h, q0;
+        decode(cur, h, q0);
+        advance(cur);
+        // step st staged, the previous step's P written and LDS reads done;
+        // then step st + 1 streams into the stage step st - 2 used (B finished
+        // with it during step st - 1)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (st + 1 < n_steps) {
+          issue_loads(pf, fill);
+          advance(pf);
         }
-      } else {
-#pragma unroll
+        const int par = st & 1;
+        bool live[2];
+        #pragma unroll
+        for (int qs = 0; qs < 2; ++qs) live[qs] = !empty_at(q0 + 32 * qs);
+        if constexpr (kA) {
+          if (live[0] && live[1]) {
+            run_a2(stg, q0, par);
+          } else {
+            #pragma unroll
+            for (int qs = 0; qs < 2; ++qs)
+              if (live[qs]) run_a(stg, qs, q0 + 32 * qs, 2 * par + qs);
+          }
+        } else {
+          #pragma unroll
+          for (int qs = 0; qs < 2; ++qs)
+            if (pend_live[qs]) run_b_dk(pend_stg, qs, 2 * pend_par + qs);
+          #pragma unroll
+          for (int qs = 0; qs < 2; ++qs)
+            if (live[qs]) run_b_dp(stg, qs);
+          pend_stg = stg;
+          pend_par = par;
+          pend_live[0] = live[0];
+          pend_live[1] = live[1];
+        }
+      };
+      for (int st = 0; st < n_steps; st += kKvStages) {  // three-stage ring: step st uses stage st % 3
+        step(st, stage0, stage1);
+        if (st + 1 < n_steps) step(st + 1, stage1, stage2);
+        if (st + 2 < n_steps) step(st + 2, stage2, stage0);
+      }
+      // B's last step
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if constexpr (!kA) {
+        #pragma unroll
         for (int qs = 0; qs < 2; ++qs)
           if (pend_live[qs]) run_b_dk(pend_stg, qs, 2 * pend_par + qs);
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-          if (live[qs]) run_b_dp(stg, qs);
-        pend_stg = stg;
-        pend_par = par;
-        pend_live[0] = live[0];
-        pend_live[1] = live[1];
       }
     };
-    for (int st = 0; st < n_steps; st += kKvStages) {  // three-stage ring: step st uses stage st % 3
-      step(st, stage0, stage1);
-      if (st + 1 < n_steps) step(st + 1, stage1, stage2);
-      if (st + 2 < n_steps) step(st + 2, stage2, stage0);
-    }
-    // B's last step
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (!kA) {
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-        if (pend_live[qs]) run_b_dk(pend_stg, qs, 2 * pend_par + qs);
-    }
-  };
-  if (roleA)
-    loop(std::true_type{});
-  else
-    loop(std::false_type{});
-  // the last steps' prefetch must land before the workgroup's LDS is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (roleA)
+      loop(std::true_type{});
+    else
+      loop(std::false_type{});
+    // the last steps' prefetch lands before the stages refill or are released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  bf16_t* const out = roleA ? dv : dk;
-  const float osc = roleA ? 1.f : scale;
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    const size_t off = (static_cast<size_t>(kbase + 16 * kh + li) * hkv + g) * D + 4 * lg;
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-      store4<bf16_t>(out + off + 16 * db, acc[db][kh][0] * osc, acc[db][kh][1] * osc,
-                     acc[db][kh][2] * osc, acc[db][kh][3] * osc);
+    bf16_t* const out = roleA ? dv : dk;
+    const float osc = roleA ? 1.f : scale;
+    #pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const size_t off = (static_cast<size_t>(kbase + 16 * kh + li) * hkv + g) * D + 4 * lg;
+      #pragma unroll
+      for (int db = 0; db < 8; ++db)
+        store4<bf16_t>(out + off + 16 * db, acc[db][kh][0] * osc, acc[db][kh][1] * osc,
+                       acc[db][kh][2] * osc, acc[db][kh][3] * osc);
+    }
   }
 }
 
@@ -564,7 +577,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   float lse2[2], dsq[2];
   // A operands K / V: key row li (+16 for the second key half), chunk 4 s + lg
   int roff[4];
-#pragma unroll
+  #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) roff[s4] = li * kRowB + (((4 * s4 + lg) ^ rsw(li)) << 4);
   int trv;  // transposed K reads: lane i of group lg addresses key 4 lg + i / 4, d = 4 (i % 4) ..
   {
@@ -574,7 +587,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   }
 
   f32x4_t dqacc[8][2];  // (d block db, query half qh)
-#pragma unroll
+  #pragma unroll
   for (int db = 0; db < 8; ++db) dqacc[db][0] = dqacc[db][1] = f32x4_t{};
 
   const uint32_t kv_bytes = static_cast<uint32_t>(hkv) * D * 2;
@@ -610,7 +623,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     if (cls == 0) return;
     // S^T and dP^T blocks (key half kh, query half qh): eight chains
     f32x4_t sacc[2][2], dpacc[2][2];
-#pragma unroll
+    #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       // dP^T accumulators start at -D of their query (all four registers of
       // a lane belong to query qlo + 16 qh + li): the MFMAs leave dP - D
@@ -622,12 +635,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     // place by scheduling barriers
     auto koffs_f = [&](int f) { return ((f & 1) ? kHalf16 : 0) + roff[f >> 1]; };
     bf16x8_t kbuf[3], vbuf[3];
-#pragma unroll
+    #pragma unroll
     for (int f = 0; f < 2; ++f) {
       kbuf[f] = lds_frag(kl, koffs_f(f));
       vbuf[f] = lds_frag(vl, koffs_f(f));
     }
-#pragma unroll
+    #pragma unroll
     for (int f = 0; f < 8; ++f) {
       if (f + 2 < 8) {
         kbuf[(f + 2) % 3] = lds_frag(kl, koffs_f(f + 2));
@@ -635,7 +648,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
       }
       __builtin_amdgcn_sched_barrier(0);
       const int s4 = f >> 1, kh = f & 1;
-#pragma unroll
+      #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
         sacc[kh][qh] = mma16(kbuf[f % 3], qf[qh][s4], sacc[kh][qh]);
         dpacc[kh][qh] = mma16(vbuf[f % 3], df[qh][s4], dpacc[kh][qh]);
@@ -653,44 +666,44 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
       const int4 s1 = *reinterpret_cast<const int4*>(sel + 16 + 4 * lg);
       const int S[2][4] = {{s0.x - kb, s0.y - kb, s0.z - kb, s0.w - kb},
                            {s1.x - kb, s1.y - kb, s1.z - kb, s1.w - kb}};
-#pragma unroll
+      #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
         const int A = qlo + 16 * qh + li - kb;
-#pragma unroll
+        #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
+          #pragma unroll
           for (int i = 0; i < 4; ++i) sacc[kh][qh][i] = A <= S[kh][i] ? sacc[kh][qh][i] : -INFINITY;
       }
       if (k0 + kQStep > qlo) {
-#pragma unroll
+        #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
           const int A = qlo + 16 * qh + li - kb;
-#pragma unroll
+          #pragma unroll
           for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
+            #pragma unroll
             for (int i = 0; i < 4; ++i) sacc[kh][qh][i] = 16 * kh + i <= A ? sacc[kh][qh][i] : -INFINITY;
         }
       }
     }
     // P = exp(S c - LSE), 0 where masked; dS = P (dP - D)
-#pragma unroll
+    #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
+      #pragma unroll
       for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
+        #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e = fast_exp2(fmaf(sacc[kh][qh][i], c, -lse2[qh]));
           dpacc[kh][qh][i] = e * dpacc[kh][qh][i];
         }
     // dQ^T += K^T.dS^T
     bf16x8_t sf[2];
-#pragma unroll
+    #pragma unroll
     for (int qh = 0; qh < 2; ++qh) sf[qh] = pack8(dpacc[0][qh], dpacc[1][qh]);
     // transposed K reads two d blocks ahead, held in place the same way
     bf16x8_t kt[3];
     kt[0] = lds_t16_frag(kl, trv, 0);
     kt[1] = lds_t16_frag(kl, trv, 1);
-#pragma unroll
+    #pragma unroll
     for (int db = 0; db < 8; ++db) {
       if (db + 2 < 8) kt[(db + 2) % 3] = lds_t16_frag(kl, trv, db + 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -711,12 +724,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   // belongs to exactly one wave of one workgroup) and written with dQ at
   // the end, for the dK/dV pass, which runs after this one (a store here
   // would hold the in-order vmcnt waits of the loop's first steps).
-#pragma unroll
+  #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
     const int row = qlo + 16 * qh + li;
     const size_t off = (static_cast<size_t>(row) * hq + h) * D + 8 * lg;
     float part = 0.f;
-#pragma unroll
+    #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       qf[qh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(q + off + 32 * s4));
       df[qh][s4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(dout + off + 32 * s4));
@@ -734,10 +747,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
     dsq[qh] = quad_sum(part);  // the four lanes of this row hold its 128 d
     lse2[qh] = lse[static_cast<size_t>(h) * tr.Np + row] * kLog2e;
   }
-#pragma unroll
+  #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
     asm volatile("" ::"v"(lse2[qh]), "v"(dsq[qh]));
-#pragma unroll
+    #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) asm volatile("" ::"v"(qf[qh][s4]), "v"(df[qh][s4]));
   }
   for (int st = 0; st < n_steps; st += 3) {  // three-stage ring: step st uses stage st % 3
@@ -748,11 +761,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(
   // the last steps' prefetch must land before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-#pragma unroll
+  #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
     if (lg == 0) dsum[static_cast<size_t>(h) * tr.Np + qlo + 16 * qh + li] = dsq[qh];
     bf16_t* op = dq + (static_cast<size_t>(qlo + 16 * qh + li) * hq + h) * D + 4 * lg;
-#pragma unroll
+    #pragma unroll
     for (int db = 0; db < 8; ++db)
       store4<bf16_t>(op + 16 * db, dqacc[db][qh][0] * scale, dqacc[db][qh][1] * scale,
                      dqacc[db][qh][2] * scale, dqacc[db][qh][3] * scale);
@@ -793,10 +806,17 @@ hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v
     launch(bwd_dq_bf16<0>);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_bf16, dim3(static_cast<unsigned>(tr.nb) * hkv), dim3(512), 0, stream,
+  // dK/dV: one persistent workgroup per CU (its LDS allows no second), as
+  // many lanes per key/value group as fill the 256 CUs, each walking its
+  // lane's list of key blocks
+  int lanes_log2 = 0;
+  while (lanes_log2 + 1 < kLaneLevels && (hkv << (lanes_log2 + 1)) <= 256) ++lanes_log2;
+  const int lanes = 1 << lanes_log2;
+  hipLaunchKernelGGL(bwd_dkdv_bf16, dim3(static_cast<unsigned>(hkv) * lanes), dim3(512), 0, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(dout), lse, dsum,
-                     static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), tr, hq, hkv, c, scale);
+                     static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), tr, hq, hkv, c, scale,
+                     lanes, lanes_log2);
   return hipGetLastError();
 }
 

@@ -19,6 +19,10 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kTile = 128;  // BLOCK_SIZE: queries and keys per tile
+// Persistent dK/dV workgroups: key-block lists for 1, 2, 4, ..., kMaxLanes
+// lanes per key/value group
+constexpr int kLaneLevels = 9;
+constexpr int kMaxLanes = 1 << (kLaneLevels - 1);
 
 // Device view of one packed tree's metadata (one device allocation; see
 // tree_meta in capi.cpp for the layout).
@@ -45,6 +49,8 @@ struct TreeDev {
   const int32_t* unit_steps;   // [n_blk32] non-empty 32x32 blocks of a unit:
                                // (32-key block << 2) | class (1 some, 2 all)
   const int32_t* unit_order;   // [Np/32] units, grouped by first key block
+  const int32_t* bwd_lanes;    // for P = 2^i lanes (i < kLaneLevels), in turn: [P+1]
+                               // lane offsets, then [nb] key blocks, lane by lane
   int32_t N;
   int32_t Np;
   int32_t nb;
