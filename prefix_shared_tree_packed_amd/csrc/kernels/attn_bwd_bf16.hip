@@ -1,8 +1,10 @@
 // Tree attention backward pass, bf16 with head_dim 128: the performance path
-// on gfx950.  Same mathematics and deterministic three-pass structure as
-// attn_bwd.hip (D = rowsum(dO*O); dK/dV per key block walking its contiguous
-// range of visible query blocks; dQ per query block over the forward tile
-// list), fed the way the forward kernel of attn_fwd_bf16.hip is fed:
+// on gfx950.  Same mathematics and deterministic result as attn_bwd.hip, in
+// two launches: first dQ per query block (or 32-query unit) over the
+// forward's step lists, which also forms D = rowsum(dO*O) for its rows;
+// then dK/dV per key block walking its contiguous range of visible query
+// blocks, in persistent workgroups.  Both are fed the way the forward
+// kernel of attn_fwd_bf16.hip is fed:
 //
 //  * Every tile reaches LDS row-major (token rows of 256 bytes) by
 //    global_load_lds_dwordx4 (no VGPRs, no VALU) through three-stage rings,
@@ -21,7 +23,7 @@
 //    dO^T.P, dK^T += Q^T.dS, dQ^T += K^T.dS^T).  Their A operands come from
 //    the same row-major tile through ds_read_b64_tr_b16: two transposing
 //    reads per MFMA operand, at nearly the rate of ordinary 16-byte reads,
-//    so no transposed copy exists anywhere and the prep pass only computes D.
+//    so no transposed copy exists anywhere.
 //  * 16-byte chunk c of tile row r sits at c ^ rsw(r), rsw(r) = 2 (r & 7) +
 //    ((r >> 3) & 1): 16 consecutive rows reading one chunk each hit 16
 //    distinct positions, and a transposing read (4 aligned rows x 2 adjacent
