@@ -808,11 +808,20 @@ hipError_t launch_attn_bwd_bf16_d128(const void* q, const void* k, const void* v
     launch(bwd_dq_bf16<0>);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dK/dV: one persistent workgroup per CU (its LDS allows no second), as
-  // many lanes per key/value group as fill the 256 CUs, each walking its
-  // lane's list of key blocks
+  // dK/dV: persistent workgroups (one per CU at a time: their LDS allows no
+  // second), each walking its lane's list of key blocks.  Lanes per
+  // key/value group: the power of two P whose hkv * P workgroups, run in
+  // rounds of 256, finish soonest if every lane carries the same work
+  // (rounds / P smallest; the fewest workgroups on ties): 32 at eight
+  // key/value heads (one workgroup per CU), 256 at five (five rounds
+  // rather than 160 of the 256 CUs busy).  More rounds than needed cost
+  // about 3 % (dispatch between workgroups).
   int lanes_log2 = 0;
-  while (lanes_log2 + 1 < kLaneLevels && (hkv << (lanes_log2 + 1)) <= 256) ++lanes_log2;
+  for (int i = 1; i < kLaneLevels; ++i) {
+    const int64_t rounds_i = (static_cast<int64_t>(hkv) * (1 << i) + 255) / 256;
+    const int64_t rounds_b = (static_cast<int64_t>(hkv) * (1 << lanes_log2) + 255) / 256;
+    if (rounds_i * (1 << lanes_log2) < rounds_b * (1 << i)) lanes_log2 = i;
+  }
   const int lanes = 1 << lanes_log2;
   hipLaunchKernelGGL(bwd_dkdv_bf16, dim3(static_cast<unsigned>(hkv) * lanes), dim3(512), 0, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
