@@ -222,7 +222,9 @@ int pst_tree_attn_fwd(const void* q, const void* k, const void* v, void* o, floa
 int pst_tree_attn_bwd_workspace_bytes(const pst_tree_meta* meta, int32_t hq, int32_t hkv,
                                       int32_t head_dim, int32_t dtype, size_t* bytes);
 
-/* Backward tree attention: gradients of sum(dout * O) with respect to q, k, v,
+/* Backward tree attention (the tree page's "Megatron 引擎" section: training
+ * through packed trees differentiates attention under the same ancestor
+ * mask as "树构建过程"): gradients of sum(dout * O) with respect to q, k, v,
  * the softmax-attention vector-Jacobian product restricted to the tree mask.
  * dk/dv sum the contributions of all query heads of their group.  `o` and
  * `lse` are the forward outputs.  dq/dk/dv are written (not accumulated), in
