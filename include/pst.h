@@ -105,8 +105,12 @@ typedef struct {
                                key sub-block ks: 0 no visible pair, 1 some, 2 all */
   int32_t* kb_qhi;          /* [n_blocks] last query block that sees each key block
                                (the visible query blocks are kb..kb_qhi[kb]) */
-  int32_t* fwd_order;       /* [n_blocks] query blocks by descending tile count */
-  int32_t* bwd_order;       /* [n_blocks] key blocks by descending tile count */
+  int32_t* fwd_order;       /* [n_blocks] query blocks by descending tile count,
+                               ties by index (a load-balancing order; the
+                               kernels schedule by orders of their own that
+                               pst_tree_meta builds at upload) */
+  int32_t* bwd_order;       /* [n_blocks] key blocks by descending tile count,
+                               ties by index (likewise) */
 } pst_tree_arrays;
 
 typedef struct {
