@@ -110,17 +110,19 @@ def test_fwd_long_sampled(gpu_lib):
 
 # ---------------------------------------------------------------- backward
 
-def _bwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, seed):
+def _bwd_full(gpu_lib, seqs, cap, hq, hkv, d, dtype, seed, scale=None, term_bound=False):
     case = Case(seqs, cap)
     try:
         for t, tree in enumerate(case.ref.trees):
-            print(f"bwd case: dtype={dtype} hq={hq} hkv={hkv} d={d} tree={t} Np={tree.n_padded}", flush=True)
+            print(f"bwd case: dtype={dtype} hq={hq} hkv={hkv} d={d} scale={scale} tree={t} "
+                  f"Np={tree.n_padded}", flush=True)
             q, k, v, do = attn_inputs(tree.n_padded, hq, hkv, d, dtype, seed + t, with_dout=True)
-            o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[t])
-            dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[t])
+            o, lse = gpu_lib.tree_attn_fwd(q, k, v, case.metas[t], softmax_scale=scale)
+            dq, dk, dv = gpu_lib.tree_attn_bwd(q, k, v, o, lse, do, case.metas[t], softmax_scale=scale)
             args = (tree, host(q), host(k), host(v), host(do))
-            rdq, rdk, rdv = oracle.attn_bwd(*args)
-            mdq, mdk, mdv = oracle.attn_bwd_magnitudes(*args) if dtype == "f32" else (None,) * 3
+            rdq, rdk, rdv = oracle.attn_bwd(*args, scale=scale)
+            mdq, mdk, mdv = (oracle.attn_bwd_magnitudes(*args, scale=scale)
+                             if dtype == "f32" or term_bound else (None,) * 3)
             assert_close(host(dq), rdq, dtype, "dQ", grad=True, mag=mdq)
             assert_close(host(dk), rdk, dtype, "dK", grad=True, mag=mdk)
             assert_close(host(dv), rdv, dtype, "dV", grad=True, mag=mdv)
@@ -143,6 +145,25 @@ def test_bwd_several_tiles(gpu_lib, dtype, hq, hkv, d):
     rng = np.random.default_rng(hq * 13 + d)
     seqs = prompt_groups(rng, 3, 150, 3, 20, 260)
     _bwd_full(gpu_lib, seqs, 1024, hq, hkv, d, dtype, 40 + hq)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.02])
+def test_fwd_bwd_softmax_scale(gpu_lib, scale):
+    """bf16 head_dim 128 (units of four heads plus 128-query blocks of the
+    fifth) at softmax scales far from 1/sqrt(d).  At 1.0 the scores span
+    tens of units in the exp2 domain, so a row's running maximum grows past
+    the forward's lazy-rescale threshold (2^8) about once per row after its
+    first block and the rescale of O and of the row sums runs; at the
+    default scale on N(0, 1) inputs it never does.  At 0.02 the softmax is
+    nearly flat.  The gradients are held to their term magnitudes: at 1.0
+    the softmax is peaked, dP - D cancels on the dominant keys, and the
+    rounding of the bf16 O that D is formed from reaches gradients an
+    absolute floor does not cover (measured: at most 0.12 %, 0.19 % and
+    0.83 % of the term magnitudes for dQ, dK and dV)."""
+    rng = np.random.default_rng(77)
+    seqs = prompt_groups(rng, 3, 150, 3, 20, 260)
+    _fwd_full(gpu_lib, seqs, 1024, 10, 2, 128, "bf16", 60, scale=scale)
+    _bwd_full(gpu_lib, seqs, 1024, 10, 2, 128, "bf16", 61, scale=scale, term_bound=True)
 
 
 def test_bwd_single_long_chain(gpu_lib):
