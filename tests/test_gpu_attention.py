@@ -48,11 +48,14 @@ def test_fwd_tiny_workload(gpu_lib):
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("f32", 4, 2, 64), ("bf16", 8, 2, 128),
                                              ("bf16", 5, 1, 64), ("bf16", 6, 6, 128),
                                              ("bf16", 10, 2, 128), ("bf16", 12, 2, 128),
-                                             ("bf16", 16, 2, 128), ("bf16", 6, 2, 128)])
+                                             ("bf16", 16, 2, 128), ("bf16", 6, 2, 128),
+                                             ("bf16", 20, 2, 128)])
 def test_fwd_several_tiles(gpu_lib, dtype, hq, hkv, d):
     """Trees spanning several 128-blocks with a ragged tail, several trees.
-    bf16 head_dim 128 with 4, 5, 6 or 8 query heads per key/value head runs
-    32-query units of several heads; 1 or 3 per group runs 128-query blocks."""
+    bf16 head_dim 128 with 4, 5, 6, 8 or 10 query heads per key/value head
+    runs 32-query units of four heads (two per group at 8 and 10, with
+    128-query blocks for the rest at 5, 6 and 10); 1 or 3 per group runs
+    128-query blocks only."""
     rng = np.random.default_rng(hq * 7 + d)
     seqs = prompt_groups(rng, 3, 150, 3, 20, 260)
     _fwd_full(gpu_lib, seqs, 1024, hq, hkv, d, dtype, 10 + hq)
@@ -138,13 +141,17 @@ def test_bwd_worked_example(gpu_lib):
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("f32", 4, 2, 64), ("bf16", 8, 2, 128),
                                              ("bf16", 5, 1, 64), ("bf16", 6, 6, 128),
                                              ("bf16", 10, 2, 128), ("bf16", 12, 2, 128),
-                                             ("bf16", 6, 2, 128)])
+                                             ("bf16", 6, 2, 128), ("bf16", 20, 2, 128)])
 def test_bwd_several_tiles(gpu_lib, dtype, hq, hkv, d):
     """Group sizes 4 (dQ in units), 1 and 3 (blocks only), 5 and 6 (units
-    for four heads of each group, blocks for the rest)."""
+    for four heads of each group, blocks for the rest), 10 (two units of
+    four heads per group, blocks for the last two).  At 10 heads per group
+    every dK/dV entry sums ten heads' separately rounded contributions, so
+    its bf16 error follows their sizes rather than |ref|: held to the term
+    magnitudes (measured 0.05 % of them for dK, 0.5 % for dV)."""
     rng = np.random.default_rng(hq * 13 + d)
     seqs = prompt_groups(rng, 3, 150, 3, 20, 260)
-    _bwd_full(gpu_lib, seqs, 1024, hq, hkv, d, dtype, 40 + hq)
+    _bwd_full(gpu_lib, seqs, 1024, hq, hkv, d, dtype, 40 + hq, term_bound=hq // hkv > 8)
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.02])
