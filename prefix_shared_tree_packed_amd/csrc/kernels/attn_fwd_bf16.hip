@@ -153,8 +153,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void tree_attn_fwd_bf16_d
   // in its L2): first the group's units, then its 128-query blocks
   const int G4 = MODE == 0 ? 0 : G / NW * NW;  // heads of each group served by units
   const int GR = G - G4;                       // heads served by 128-query blocks
-  const int per_unit = MODE == 0 ? 1 : G4 / NW;  // unit workgroups per unit and group (1: unused)
-  const int u_g = per_unit * (tr.Np / 32);
+  const int per_unit = MODE == 0 ? 1 : G4 / NW;  // unit workgroups per unit and group
+  const int u_g = MODE == 0 ? 0 : per_unit * (tr.Np / 32);  // unit workgroups per group
   const int per_g = u_g + GR * tr.nb;
   const int g = logical / per_g;
   const int rem = logical - g * per_g;
