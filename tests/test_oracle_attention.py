@@ -136,18 +136,20 @@ def test_bwd_finite_differences():
             assert grad[i, h, c] == pytest.approx(fd, abs=1e-7, rel=1e-6), (name, i, h, c)
 
 
-@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 1), (6, 3)])
-def test_bwd_equals_autograd_of_causal(hq, hkv):
+@pytest.mark.parametrize("hq,hkv,scale", [(2, 2, None), (4, 1, None), (6, 3, None),
+                                          (4, 2, 1.0), (4, 2, 0.05)])
+def test_bwd_equals_autograd_of_causal(hq, hkv, scale):
     """Loss = sum over packed real rows of <dO_i, O_i>.  Each packed row is
     represented by one (sequence, position) that reaches it; autograd through
     the per-sequence causal attention and the index gathers must give the
-    packed gradients.  Pad rows: dV = dO, dQ = dK = 0."""
+    packed gradients, at the default softmax scale and at others.  Pad rows:
+    dV = dO, dQ = dK = 0."""
     rng = np.random.default_rng(hq + 10 * hkv)
     d = 8
     seqs = _random_seqs(rng)
     tree = oracle.build_forest(seqs, 256).trees[0]
     q, k, v, do = _tree_inputs(tree, hq, hkv, d, 2)
-    dq, dk, dv = oracle.attn_bwd(tree, q, k, v, do)
+    dq, dk, dv = oracle.attn_bwd(tree, q, k, v, do, scale=scale)
     N = tree.n_tokens
     Q = torch.tensor(q, requires_grad=True)
     K = torch.tensor(k, requires_grad=True)
@@ -162,7 +164,7 @@ def test_bwd_equals_autograd_of_causal(hq, hkv):
         Qs = Q[idx].permute(1, 0, 2)
         Ks = K[idx].permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
         Vs = V[idx].permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
-        Os = F.scaled_dot_product_attention(Qs, Ks, Vs, is_causal=True).permute(1, 0, 2)
+        Os = F.scaled_dot_product_attention(Qs, Ks, Vs, is_causal=True, scale=scale).permute(1, 0, 2)
         w = np.zeros((len(idx), hq, d))
         for t, i in enumerate(tree.seq_index[sid]):
             if owner[int(i)] == (sid, t):
@@ -223,11 +225,12 @@ def _magnitudes_brute_force(tree, q, k, v, do, s):
     return mq, mk, mv
 
 
-def test_bwd_magnitudes_brute_force():
+@pytest.mark.parametrize("scale", [None, 1.0])
+def test_bwd_magnitudes_brute_force(scale):
     tree = oracle.build_forest(worked_example_edge() + [np.array([1, 2, 9], np.int32)], 128).trees[0]
     q, k, v, do = _tree_inputs(tree, 4, 2, 3, 12)
-    got = oracle.attn_bwd_magnitudes(tree, q, k, v, do)
-    exp = _magnitudes_brute_force(tree, q, k, v, do, 1 / np.sqrt(3))
+    got = oracle.attn_bwd_magnitudes(tree, q, k, v, do, scale=scale)
+    exp = _magnitudes_brute_force(tree, q, k, v, do, 1 / np.sqrt(3) if scale is None else scale)
     for a, b in zip(got, exp):
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
 
