@@ -402,6 +402,13 @@ int pst_pack_metrics_compute(const int64_t* values, int32_t n, const int32_t* gr
 /* Message of the last failed call on this thread ("" if none). */
 const char* pst_last_error(void);
 
+/* SHA-256, in hex, of the sources this library was built from (its C++ and
+ * HIP sources, the headers under include/ and the build script), or
+ * "unknown" for a build that did not record it.  A loader compares it with
+ * the sources at hand to refuse a library built from other ones.  The
+ * string is static; the call never fails. */
+const char* pst_build_sources_sha256(void);
+
 #ifdef __cplusplus
 }
 #endif

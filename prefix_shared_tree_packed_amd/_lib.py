@@ -106,6 +106,7 @@ _SIGS = {
     "pst_build_tree_ex": (c_int32, [P32, P64, c_int32, c_int32, c_int32, POINTER(c_void_p)]),
     "pst_tree_dense_mask": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
     "pst_last_error": (c_char_p, []),
+    "pst_build_sources_sha256": (c_char_p, []),
 }
 
 _lib = None
@@ -118,9 +119,18 @@ def header_functions():
     return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(pst_\w+)\s*\(", text, re.M)))
 
 
+def verify_build(lib, want: str) -> None:
+    """Raise unless `lib` was built from the sources whose digest is `want`."""
+    got = lib.pst_build_sources_sha256().decode()
+    if got != want:
+        raise RuntimeError(f"libpst was built from other sources (digest {got[:16]}, sources "
+                           f"{want[:16]}); rebuild: python -m prefix_shared_tree_packed_amd.build")
+
+
 def load(path: str = LIB_PATH):
-    """Load libpst.so (built in-tree).  Raises if it is missing: there is no
-    fallback implementation."""
+    """Load libpst.so (built in-tree).  Raises if it is missing (there is no
+    fallback implementation) or, for the in-tree library, if it was built
+    from sources other than the ones in the tree."""
     global _lib
     if _lib is not None:
         return _lib
@@ -135,6 +145,9 @@ def load(path: str = LIB_PATH):
             continue
         fn.restype = res
         fn.argtypes = args
+    if path == os.path.join(PKG, "libpst.so"):
+        from .build import sources_sha256
+        verify_build(lib, sources_sha256())
     _lib = lib
     return lib
 

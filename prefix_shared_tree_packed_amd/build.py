@@ -56,6 +56,27 @@ SAN_FLAGS = ["-O1", "-g", "-std=c++17", "-fPIC", "-Wall", "-fno-omit-frame-point
              f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+def sources_sha256(root: str = ROOT) -> str:
+    """SHA-256 of the library's own sources under the repository root `root`
+    (C++/HIP under the package's csrc/, the headers under include/, this
+    script), each under its path relative to `root`.  Compiled into the
+    library (pst_build_sources_sha256), so that a loader can tell a library
+    built from other sources."""
+    import hashlib
+    pkg = os.path.join(root, os.path.basename(PKG))
+    files = [os.path.join(dp, f) for dp, _, fs in os.walk(os.path.join(pkg, "csrc")) for f in fs
+             if f.endswith((".cpp", ".h", ".hip"))]
+    inc = os.path.join(root, "include")
+    files += [os.path.join(inc, f) for f in os.listdir(inc) if f.endswith(".h")]
+    files.append(os.path.join(pkg, "build.py"))
+    h = hashlib.sha256()
+    for path in sorted(os.path.relpath(f, root).replace(os.sep, "/") for f in files):
+        h.update(path.encode() + b"\0")
+        with open(os.path.join(root, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def _hipcc() -> str:
     for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if c and os.path.exists(c):
@@ -87,9 +108,10 @@ def build(verbose: bool = False) -> str:
         jobs.append([hipcc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src),
                      "-o", obj])
         objs.append(obj)
+    digest = f'-DPST_SOURCES_SHA256="{sources_sha256()}"'
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
-        jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append(["g++", *CXX_FLAGS, digest, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
@@ -107,7 +129,8 @@ def build_host_sanitized(verbose: bool = False) -> str:
     os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in CXX_SOURCES]
     tmp = SAN_LIB + ".tmp"
-    _run(["g++", *SAN_FLAGS, "-shared", *srcs, "-o", tmp], verbose)
+    _run(["g++", *SAN_FLAGS, f'-DPST_SOURCES_SHA256="{sources_sha256()}"', "-shared", *srcs, "-o", tmp],
+         verbose)
     os.replace(tmp, SAN_LIB)
     return SAN_LIB
 

@@ -132,6 +132,12 @@ int pst_pack_metrics_compute(const int64_t* values, int32_t n, const int32_t* gr
 
 const char* pst_last_error(void) { return pst::last_error(); }
 
+// the build script passes the digest of the sources it compiles
+#ifndef PST_SOURCES_SHA256
+#define PST_SOURCES_SHA256 "unknown"
+#endif
+const char* pst_build_sources_sha256(void) { return PST_SOURCES_SHA256; }
+
 int pst_build_tree_ex(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
                       int32_t max_tokens_per_mb, int32_t flags, pst_forest** out) {
   if (!out) return fail(PST_EINVAL, "out is NULL");

@@ -19,6 +19,31 @@ def test_exports_every_declared_function():
     assert set(names) == set(_lib._SIGS), "binding and header disagree"
 
 
+def test_library_built_from_the_sources_in_the_tree(tmp_path):
+    """The in-tree library records the digest of the sources it was built
+    from, equal to that of the sources at hand (a stale build would have
+    been refused by load()); a digest that differs is refused, and an edit
+    to any source changes the digest."""
+    from prefix_shared_tree_packed_amd import build
+    lib = pst.load()
+    want = build.sources_sha256()
+    assert lib.pst_build_sources_sha256().decode() == want
+    _lib.verify_build(lib, want)
+    with pytest.raises(RuntimeError, match="other sources"):
+        _lib.verify_build(lib, "0" * 64)
+    # the same sources elsewhere give the same digest; one byte more does not
+    import os
+    import shutil
+    pkg = os.path.basename(build.PKG)
+    shutil.copytree(build.CSRC, tmp_path / pkg / "csrc", ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copy(os.path.join(build.PKG, "build.py"), tmp_path / pkg / "build.py")
+    shutil.copytree(build.INCLUDE, tmp_path / "include")
+    assert build.sources_sha256(str(tmp_path)) == want
+    with open(tmp_path / pkg / "csrc" / "kernels" / "common.h", "ab") as f:
+        f.write(b"\n")
+    assert build.sources_sha256(str(tmp_path)) != want
+
+
 def test_device_entry_points_reject_null_meta():
     lib = pst.load()
     p = ctypes.c_void_p(16)
